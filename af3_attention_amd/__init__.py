@@ -1,0 +1,14 @@
+"""MI355X-native memory-efficient 3D attention with an additively broadcast pair bias.
+
+The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
+declared in include/evoattn.h; this package is the thin Python binding.
+"""
+from .evoattn import (  # noqa: F401
+    EvoAttnFunction,
+    evoattn,
+    evoattn_bwd,
+    evoattn_bwd_workspace_bytes,
+    evoattn_fwd,
+    evoattn_fwd_workspace_bytes,
+)
+from ._lib import EvoAttnError, LIB_PATH  # noqa: F401

@@ -1,0 +1,182 @@
+// C entry points of the EvoAttention library: argument validation, workspace
+// layout and kernel dispatch.  Declared in include/evoattn.h.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "evoattn.h"
+#include "evoattn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+evoattn_status_t fail(evoattn_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validates sizes and enums; fills `p`.
+evoattn_status_t check_problem(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype,
+                               int transpose, evo::Problem* p) {
+  if (rows < 1 || n < 1 || heads < 1 || head_dim < 1)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (rows=%lld n=%lld heads=%lld head_dim=%lld)",
+                (long long)rows, (long long)n, (long long)heads, (long long)head_dim);
+  if (dtype != EVOATTN_FP32 && dtype != EVOATTN_BF16)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "dtype %d is not EVOATTN_FP32 or EVOATTN_BF16", dtype);
+  if (transpose != 0 && transpose != 1)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "transpose must be 0 or 1, got %d", transpose);
+  if (head_dim != 8 && head_dim != 16 && head_dim != 32 && head_dim != 64)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (8, 16, 32, 64)", (long long)head_dim);
+  const double elems = static_cast<double>(rows) * n * heads * head_dim;
+  const double bias_elems = static_cast<double>(heads) * n * n;
+  if (elems >= 2147483648.0 || bias_elems >= 2147483648.0)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "problem too large: R*N*H*d=%.0f, H*N*N=%.0f (limit 2^31 each)", elems,
+                bias_elems);
+  if (p) {
+    p->R = static_cast<int>(rows);
+    p->N = static_cast<int>(n);
+    p->H = static_cast<int>(heads);
+    p->D = static_cast<int>(head_dim);
+    p->dtype = dtype;
+    p->transpose = transpose;
+    p->row_stride = transpose ? 1 : n;
+    p->pos_stride = transpose ? rows : 1;
+    p->scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(head_dim)));
+  }
+  return EVOATTN_OK;
+}
+
+#define REQUIRE_PTR(ptr, align)                                                                          \
+  do {                                                                                                   \
+    if (!(ptr)) return fail(EVOATTN_ERR_INVALID_ARGUMENT, "%s must not be NULL", #ptr);                   \
+    if (!aligned((ptr), (align)))                                                                        \
+      return fail(EVOATTN_ERR_INVALID_ARGUMENT, "%s must be %d-byte aligned", #ptr, (int)(align));        \
+  } while (0)
+
+#define OPTIONAL_PTR(ptr, align)                                                                         \
+  do {                                                                                                   \
+    if ((ptr) && !aligned((ptr), (align)))                                                               \
+      return fail(EVOATTN_ERR_INVALID_ARGUMENT, "%s must be %d-byte aligned", #ptr, (int)(align));        \
+  } while (0)
+
+evoattn_status_t check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+  return EVOATTN_OK;
+}
+
+size_t bwd_ws_bytes(const evo::Problem& p) {
+  const size_t delta = static_cast<size_t>(p.R) * p.H * p.N * sizeof(float);
+  return round_up(delta);
+}
+
+}  // namespace
+
+extern "C" {
+
+int evoattn_abi_version(void) { return EVOATTN_ABI_VERSION; }
+
+const char* evoattn_status_string(int status) {
+  switch (status) {
+    case EVOATTN_OK: return "EVOATTN_OK";
+    case EVOATTN_ERR_INVALID_ARGUMENT: return "EVOATTN_ERR_INVALID_ARGUMENT";
+    case EVOATTN_ERR_UNSUPPORTED: return "EVOATTN_ERR_UNSUPPORTED";
+    case EVOATTN_ERR_WORKSPACE: return "EVOATTN_ERR_WORKSPACE";
+    case EVOATTN_ERR_DEVICE: return "EVOATTN_ERR_DEVICE";
+    default: return "EVOATTN_UNKNOWN_STATUS";
+  }
+}
+
+const char* evoattn_last_error_detail(void) { return g_last_error.c_str(); }
+
+size_t evoattn_fwd_workspace_bytes(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype) {
+  evo::Problem p;
+  if (check_problem(rows, n, heads, head_dim, dtype, 0, &p) != EVOATTN_OK) return 0;
+  return 0;
+}
+
+size_t evoattn_bwd_workspace_bytes(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype) {
+  evo::Problem p;
+  if (check_problem(rows, n, heads, head_dim, dtype, 0, &p) != EVOATTN_OK) return 0;
+  return bwd_ws_bytes(p);
+}
+
+evoattn_status_t evoattn_fwd(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype, int transpose,
+                             const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                             void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  evo::Problem p;
+  evoattn_status_t st = check_problem(rows, n, heads, head_dim, dtype, transpose, &p);
+  if (st != EVOATTN_OK) return st;
+  REQUIRE_PTR(q, 16);
+  REQUIRE_PTR(k, 16);
+  REQUIRE_PTR(v, 16);
+  REQUIRE_PTR(o, 16);
+  OPTIONAL_PTR(bias, 16);
+  OPTIONAL_PTR(mask, 4);
+  OPTIONAL_PTR(lse, 4);
+  if ((st = check_device()) != EVOATTN_OK) return st;
+
+  evo::FwdArgs a{q, k, v, bias, mask, o, lse};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = evo::launch_fwd_vector(p, a, s);
+  if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return EVOATTN_OK;
+}
+
+evoattn_status_t evoattn_bwd(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype, int transpose,
+                             const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                             const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  evo::Problem p;
+  evoattn_status_t st = check_problem(rows, n, heads, head_dim, dtype, transpose, &p);
+  if (st != EVOATTN_OK) return st;
+  REQUIRE_PTR(q, 16);
+  REQUIRE_PTR(k, 16);
+  REQUIRE_PTR(v, 16);
+  REQUIRE_PTR(o, 16);
+  REQUIRE_PTR(lse, 4);
+  REQUIRE_PTR(dout, 16);
+  REQUIRE_PTR(dq, 16);
+  REQUIRE_PTR(dk, 16);
+  REQUIRE_PTR(dv, 16);
+  OPTIONAL_PTR(bias, 16);
+  OPTIONAL_PTR(mask, 4);
+  OPTIONAL_PTR(dbias, 4);
+  const size_t need = bwd_ws_bytes(p);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(EVOATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu at %p", need, workspace_bytes, workspace);
+  if (workspace && !aligned(workspace, 256))
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if ((st = check_device()) != EVOATTN_OK) return st;
+
+  evo::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.bias = bias; a.mask = mask; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dbias = dbias;
+  a.delta = static_cast<float*>(workspace);
+  a.scratch = nullptr;
+  a.scratch_bytes = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = evo::launch_bwd_vector(p, a, s);
+  if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return EVOATTN_OK;
+}
+
+}  // extern "C"

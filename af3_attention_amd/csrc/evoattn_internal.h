@@ -1,0 +1,89 @@
+// Internal declarations shared by the host entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace evo {
+
+// Problem description handed to every kernel launcher.  Element (r, p, h, c)
+// of q/k/v/o/dout/dq/dk/dv lives at ((r*row_stride + p*pos_stride)*H + h)*D + c,
+// so transpose only changes the two strides.
+struct Problem {
+  int R, N, H, D;
+  int dtype;          // 0 fp32, 1 bf16
+  int transpose;
+  int64_t row_stride; // in positions: N when transpose == 0, 1 otherwise
+  int64_t pos_stride; // in positions: 1 when transpose == 0, R otherwise
+  float scale;        // 1/sqrt(D)
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;   // [H,N,N] or nullptr
+  const float* mask;  // [R,N] or nullptr
+  void* o;
+  float* lse;         // [R,H,N] or nullptr
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;
+  const float* mask;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dbias;       // [H,N,N] or nullptr
+  float* delta;       // workspace [R,H,N]: sum_c dout*o per softmax row
+  float* scratch;     // further workspace (path specific)
+  size_t scratch_bytes;
+};
+
+// Brackets one kernel launch with HIP events on its stream while timing is
+// enabled (evoattn_timing_enable); a no-op otherwise.
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t stream);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
+};
+
+// Vector-ALU path: any supported head_dim, fp32 or bf16 storage, fp32 math.
+hipError_t launch_fwd_vector(const Problem& p, const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_vector(const Problem& p, const BwdArgs& a, hipStream_t s);
+
+// bf16 storage conversions (round to nearest even; NaN stays NaN).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+}  // namespace evo

@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Throughput of pair-biased 3D attention (forward + backward) on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+evoattn_fwd (O, lse) followed by evoattn_bwd (dQ, dK, dV, dBias), with every
+input already resident in HBM.  The default workload is starting-node
+triangle attention at an AF3 training crop: N = 384 rows and positions, H = 4
+heads, d = 32, bf16 storage with fp32 accumulation, bias ~ N(0, 2), tail key
+mask.  Flops are counted as 4*R*N^2*H*d for the forward and 10*R*N^2*H*d for
+the backward (five N x N x d contractions, one of them the recompute of
+Q K^T).
+
+Prints one JSON line.  Besides the throughput it reports
+  roofline      the kernel with the largest share of the step: algorithmic
+                flops (or bytes) per launch divided by its mean launch time,
+                measured with HIP events recorded by the library on the launch
+                stream inside the timed region, against the MI355X peak;
+  cpu_baseline  the fp64 CPU oracle timed on this host's cores on a bounded
+                sample of rows of the same workload (skip with --no-cpu-baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "fwd+bwd TFLOP/s (% bf16 MFMA peak), triangle attn N=384 H=4 d=32"
+UNIT = "TFLOP/s"
+
+# MI355X published peaks.
+PEAK_BF16_MFMA_TFLOPS = 2500.0   # dense bf16 matrix
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # fp32 vector ALU
+PEAK_HBM_GBS = 8000.0
+
+# Algorithmic work per launch of each kernel, in multiples of R*N^2*H*d flops
+# (score elements times head_dim), with the unit that bounds it.
+KERNEL_FLOP_FACTOR = {
+    "fwd_mfma": (4.0, "mfma"),
+    "bwd_mfma": (10.0, "mfma"),
+    "bwd_dkdv_mfma": (8.0, "mfma"),
+    "bwd_dq_mfma": (6.0, "mfma"),
+    "fwd_vector": (4.0, "alu"),
+    "bwd_dq_vector": (6.0, "alu"),
+    "bwd_dkdv_vector": (8.0, "alu"),
+    "bwd_dbias_vector": (4.0, "alu"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="tri_start_bf16_n384")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, target_s):
+    """Time the fp64 oracle (fwd + bwd) on a sample of rows sized to ~target_s seconds."""
+    import numpy as np
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    used = oracle.set_threads(threads)
+    to64 = lambda t: None if t is None else t.detach().cpu().double().numpy()
+    q, k, v, b, m, do = (to64(inp[x]) for x in ("q", "k", "v", "bias", "mask", "dout"))
+    t = inp["transpose"]
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.fwd(q, k, v, b, m, t, rows=rows)
+        oracle.bwd(q, k, v, b, m, do, t, rows=rows)
+        return time.perf_counter() - t0
+
+    probe = run([0])
+    nrows = int(max(1, min(w.rows, target_s / max(probe, 1e-6))))
+    rows = list(range(nrows))
+    secs = run(rows) if nrows > 1 else probe
+    per_row_flops = 14.0 * w.n * w.n * w.heads * w.head_dim
+    value = per_row_flops * nrows / secs / 1e12
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": value, "unit": UNIT, "cores": used, "kind": "oracle",
+        "sample": f"rows 0..{nrows - 1} of {w.rows} of {w.name} (fwd+bwd, fp64), {secs:.2f} s",
+        "seconds": secs, "cpu_model": cpu_model,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import af3_attention_amd as ea
+    from af3_attention_amd import _lib
+    from workloads import WORKLOADS, generate_workload
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    variants = list(w.variants) if len(w.variants) > 1 else [w.transpose]
+    inputs_cpu = [generate_workload(w, transpose=t, seed=args.seed + i) for i, t in enumerate(variants)]
+    inputs = [{x: (v.to(dev) if torch.is_tensor(v) else v) for x, v in inp.items()} for inp in inputs_cpu]
+    torch.cuda.synchronize()
+
+    def step():
+        saved = []
+        for inp in inputs:
+            o, lse = ea.evoattn_fwd(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], bool(inp["transpose"]))
+            saved.append((o, lse))
+        for inp, (o, lse) in reversed(list(zip(inputs, saved))):
+            ea.evoattn_bwd(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], o, lse, inp["dout"],
+                           bool(inp["transpose"]))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_mem = torch.cuda.memory_allocated(dev)
+
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _lib.timing_collect()          # drop anything recorded before
+    _lib.timing_enable(True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    _lib.timing_enable(False)
+    kernels = _lib.timing_collect()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem
+
+    flops_step = w.flops_fwd_bwd() * len(variants)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # Roofline of the dominant kernel.
+    dom = max(kernels.items(), key=lambda kv: kv[1][1]) if kernels else None
+    roofline = None
+    if dom:
+        name, (count, tot) = dom
+        avg_ms = tot / count
+        factor, bound = KERNEL_FLOP_FACTOR.get(name, (None, None))
+        launches_per_step = count / args.steps
+        units = w.rows * w.n * w.n * w.heads * w.head_dim * len(variants) / launches_per_step
+        if factor is not None:
+            achieved = factor * units / (avg_ms * 1e-3) / 1e12
+            peak = PEAK_BF16_MFMA_TFLOPS if bound == "mfma" else PEAK_FP32_VECTOR_TFLOPS
+            roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                        "frac": achieved / peak, "traffic": None, "kernel": name,
+                        "avg_launch_ms": avg_ms, "launches": count}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inputs_cpu[0], args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "n": w.n, "heads": w.heads, "head_dim": w.head_dim,
+                   "transpose": variants, "mask": w.mask_kind, "seed": args.seed},
+        "frac_of_bf16_peak": value / PEAK_BF16_MFMA_TFLOPS,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_ms_per_step": {k: tot / args.steps for k, (c, tot) in kernels.items()},
+        "peak_hbm_extra_bytes": int(peak_extra),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+"""Boundary tests that need no GPU: the C header, the exported symbols and the
+argument validation that runs before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from af3_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "evoattn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, DEVICE = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(evoattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "evoattn.h"\nint main(void){return evoattn_abi_version() == EVOATTN_ABI_VERSION ? 0 : 1;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
+                    str(src)], check=True)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (evoattn_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.evoattn_abi_version() == 1
+    for code, name in ((OK, "EVOATTN_OK"), (INVALID, "EVOATTN_ERR_INVALID_ARGUMENT"),
+                       (UNSUPPORTED, "EVOATTN_ERR_UNSUPPORTED"), (WORKSPACE, "EVOATTN_ERR_WORKSPACE"),
+                       (DEVICE, "EVOATTN_ERR_DEVICE")):
+        assert lib.evoattn_status_string(code).decode() == name
+    assert lib.evoattn_status_string(99).decode() == "EVOATTN_UNKNOWN_STATUS"
+
+
+def test_workspace_queries():
+    lib = _lib.load()
+    assert lib.evoattn_fwd_workspace_bytes(384, 384, 4, 32, 1) == 0
+    ws = lib.evoattn_bwd_workspace_bytes(384, 384, 4, 32, 1)
+    assert ws >= 384 * 4 * 384 * 4            # at least the per-row statistics
+    assert ws % 256 == 0
+    # O(R*H*N + H*N*N): far below one N^3 score tensor
+    assert ws < 384 * 384 * 384 * 4 * 2 / 8
+    assert lib.evoattn_bwd_workspace_bytes(0, 384, 4, 32, 1) == 0       # invalid -> 0
+    assert lib.evoattn_bwd_workspace_bytes(8, 8, 4, 24, 1) == 0         # unsupported d -> 0
+
+
+# Fake, aligned, never dereferenced addresses: every call below must fail validation
+# before anything touches a device.
+A = 1 << 20
+
+
+def fwd(**kw):
+    lib = _lib.load()
+    args = dict(rows=4, n=8, heads=2, head_dim=32, dtype=1, transpose=0, q=A, k=A, v=A, bias=None, mask=None,
+                o=A, lse=A, ws=None, ws_bytes=0)
+    args.update(kw)
+    return lib.evoattn_fwd(args["rows"], args["n"], args["heads"], args["head_dim"], args["dtype"],
+                           args["transpose"], args["q"], args["k"], args["v"], args["bias"], args["mask"],
+                           args["o"], args["lse"], args["ws"], args["ws_bytes"], None)
+
+
+def bwd(**kw):
+    lib = _lib.load()
+    args = dict(rows=4, n=8, heads=2, head_dim=32, dtype=1, transpose=0, q=A, k=A, v=A, bias=None, mask=None,
+                o=A, lse=A, dout=A, dq=A, dk=A, dv=A, dbias=None, ws=A, ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.evoattn_bwd(args["rows"], args["n"], args["heads"], args["head_dim"], args["dtype"],
+                           args["transpose"], args["q"], args["k"], args["v"], args["bias"], args["mask"],
+                           args["o"], args["lse"], args["dout"], args["dq"], args["dk"], args["dv"],
+                           args["dbias"], args["ws"], args["ws_bytes"], None)
+
+
+def detail():
+    return _lib.load().evoattn_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(rows=0), INVALID, "sizes"),
+    (dict(n=-1), INVALID, "sizes"),
+    (dict(heads=0), INVALID, "sizes"),
+    (dict(dtype=7), INVALID, "dtype"),
+    (dict(transpose=2), INVALID, "transpose"),
+    (dict(head_dim=24), UNSUPPORTED, "head_dim"),
+    (dict(head_dim=128), UNSUPPORTED, "head_dim"),
+    (dict(rows=1 << 20, n=1 << 10, heads=8, head_dim=64), UNSUPPORTED, "too large"),
+    (dict(q=None), INVALID, "q must not be NULL"),
+    (dict(v=None), INVALID, "v must not be NULL"),
+    (dict(o=None), INVALID, "o must not be NULL"),
+    (dict(k=A + 2), INVALID, "aligned"),
+    (dict(bias=A + 8), INVALID, "aligned"),
+    (dict(mask=A + 2), INVALID, "aligned"),
+])
+def test_fwd_validation(kw, code, needle):
+    assert fwd(**kw) == code
+    assert needle in detail()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(rows=-3), INVALID, "sizes"),
+    (dict(head_dim=12), UNSUPPORTED, "head_dim"),
+    (dict(lse=None), INVALID, "lse must not be NULL"),
+    (dict(dout=None), INVALID, "dout must not be NULL"),
+    (dict(dq=None), INVALID, "dq must not be NULL"),
+    (dict(dk=None), INVALID, "dk must not be NULL"),
+    (dict(dv=None), INVALID, "dv must not be NULL"),
+    (dict(dbias=A + 1), INVALID, "aligned"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(ws_bytes=16), WORKSPACE, "workspace"),
+    (dict(ws=A + 64), INVALID, "256-byte"),
+])
+def test_bwd_validation(kw, code, needle):
+    assert bwd(**kw) == code
+    assert needle in detail()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful where no GPU is present")
+def test_valid_call_without_device_reports_device_error():
+    """A call that passes validation on a machine without a GPU returns EVOATTN_ERR_DEVICE and
+    launches nothing (the addresses are fake)."""
+    assert fwd() == DEVICE
+    assert "device" in detail().lower()
+
+
+def test_python_binding_rejects_bad_tensors():
+    import af3_attention_amd as ea
+    q = torch.zeros(2, 3, 1, 8)
+    with pytest.raises(ValueError):
+        ea.evoattn_fwd(q, q, q)          # CPU tensors are rejected before any library call

@@ -79,7 +79,13 @@ evoattn_status_t check_device() {
   return EVOATTN_OK;
 }
 
+// fp32 storage runs the vector-ALU kernels; bf16 storage runs the MFMA kernels.
+bool use_mfma(const evo::Problem& p) { return p.dtype == EVOATTN_BF16; }
+
+size_t fwd_ws_bytes(const evo::Problem& p) { return use_mfma(p) ? round_up(evo::fwd_mfma_workspace_bytes(p)) : 0; }
+
 size_t bwd_ws_bytes(const evo::Problem& p) {
+  if (use_mfma(p)) return round_up(evo::bwd_mfma_workspace_bytes(p));
   const size_t delta = static_cast<size_t>(p.R) * p.H * p.N * sizeof(float);
   return round_up(delta);
 }
@@ -106,7 +112,7 @@ const char* evoattn_last_error_detail(void) { return g_last_error.c_str(); }
 size_t evoattn_fwd_workspace_bytes(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype) {
   evo::Problem p;
   if (check_problem(rows, n, heads, head_dim, dtype, 0, &p) != EVOATTN_OK) return 0;
-  return 0;
+  return fwd_ws_bytes(p);
 }
 
 size_t evoattn_bwd_workspace_bytes(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype) {
@@ -118,8 +124,6 @@ size_t evoattn_bwd_workspace_bytes(int64_t rows, int64_t n, int64_t heads, int64
 evoattn_status_t evoattn_fwd(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype, int transpose,
                              const void* q, const void* k, const void* v, const void* bias, const float* mask,
                              void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   evo::Problem p;
   evoattn_status_t st = check_problem(rows, n, heads, head_dim, dtype, transpose, &p);
   if (st != EVOATTN_OK) return st;
@@ -130,11 +134,16 @@ evoattn_status_t evoattn_fwd(int64_t rows, int64_t n, int64_t heads, int64_t hea
   OPTIONAL_PTR(bias, 16);
   OPTIONAL_PTR(mask, 4);
   OPTIONAL_PTR(lse, 4);
+  const size_t need = fwd_ws_bytes(p);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(EVOATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu at %p", need, workspace_bytes, workspace);
+  if (workspace && !aligned(workspace, 256))
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   if ((st = check_device()) != EVOATTN_OK) return st;
 
   evo::FwdArgs a{q, k, v, bias, mask, o, lse};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = evo::launch_fwd_vector(p, a, s);
+  hipError_t e = use_mfma(p) ? evo::launch_fwd_mfma(p, a, workspace, s) : evo::launch_fwd_vector(p, a, s);
   if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return EVOATTN_OK;
@@ -173,7 +182,7 @@ evoattn_status_t evoattn_bwd(int64_t rows, int64_t n, int64_t heads, int64_t hea
   a.scratch = nullptr;
   a.scratch_bytes = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = evo::launch_bwd_vector(p, a, s);
+  hipError_t e = use_mfma(p) ? evo::launch_bwd_mfma(p, a, workspace, s) : evo::launch_bwd_vector(p, a, s);
   if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return EVOATTN_OK;

@@ -65,6 +65,13 @@ class KernelTimer {
 hipError_t launch_fwd_vector(const Problem& p, const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_vector(const Problem& p, const BwdArgs& a, hipStream_t s);
 
+// bf16 MFMA path (gfx950 matrix cores), fp32 accumulation.  Workspace sizes in
+// bytes; the launchers carve their scratch out of `ws`.
+size_t fwd_mfma_workspace_bytes(const Problem& p);
+size_t bwd_mfma_workspace_bytes(const Problem& p);
+hipError_t launch_fwd_mfma(const Problem& p, const FwdArgs& a, void* ws, hipStream_t s);
+hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& a, void* ws, hipStream_t s);
+
 // bf16 storage conversions (round to nearest even; NaN stays NaN).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

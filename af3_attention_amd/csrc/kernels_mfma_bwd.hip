@@ -1,0 +1,577 @@
+// bf16 MFMA backward of pair-biased 3D attention for gfx950.
+//
+// The backward recomputes the softmax from the saved per-row logsumexp
+// instead of storing the R*H*N*N probabilities (the pages' memory-efficient
+// kernel runs in the forward and the backward pass: gist.science MegaFold
+// technical summary, Methodik section 1 "EvoFlash-3D").  With dS = P * (dP - D),
+// D[j] = sum_c dO[j,c] O[j,c], the gradients are
+//   dV = P^T dO,  dK = dS^T Q / sqrt(d),  dQ = dS K / sqrt(d),
+//   dBias[h,j,k] = sum over rows r of dS[r,h,j,k].
+//
+// Three kernels each own complete outputs, so nothing is accumulated with
+// atomics and every sum has a fixed order:
+//  * dkdv : workgroup = 128 keys (4 waves x 32) of one (row, head); walks the
+//           queries in steps of 64.  Tiles are S = Q K^T (queries x keys): each
+//           lane holds one key, so P and dS in registers are directly the B
+//           operands of dV^T = dO^T P and dK^T = Q^T dS.
+//  * dq   : workgroup = 128 queries of one (row, head); walks the keys in steps
+//           of 64 with the forward's transposed tiles S^T = K Q^T, so dS^T in
+//           registers is the B operand of dQ^T = K^T dS^T.
+//  * dbias: workgroup = a 64 x 128 (query x key) tile of one head; walks a group
+//           of rows in increasing order and sums dS in registers.  Row groups
+//           give partial sums that a last kernel adds in increasing group order.
+// Scaled bias (sqrt(d) * bias, fp32) initialises every S accumulator and -D
+// initialises every dP accumulator, so neither costs vector ALU work.
+
+#include <algorithm>
+
+#include "mfma_common.h"
+
+namespace evo {
+namespace {
+
+using namespace mfma;
+
+constexpr int kThreads = 256;
+constexpr int kStep = 64;  // queries (dkdv, dbias) or keys (dq) staged per step
+
+template <int D>
+struct Shape {
+  static constexpr int KS = D >= 16 ? D / 16 : 1;  // 16-deep steps over d
+  static constexpr int DB = D >= 32 ? D / 32 : 1;  // 32-row blocks over d for transposed outputs
+  static constexpr int ROW = KS * 16 + 8;          // bf16 per staged [pos][d] row (8 padding)
+  static constexpr int TROW = kStep + 8;           // bf16 per staged [d][pos] row (8 padding)
+  static constexpr int CHUNKS = D / 8;             // 16-byte chunks per position
+};
+
+// Stage kStep positions starting at p0 of one (row, head) of `src` into LDS:
+// row-major [pos][d] (if rows != nullptr) and transposed [d][pos] (if trans != nullptr).
+// Positions >= N are zero.
+template <int D>
+__device__ __forceinline__ void stage(const Problem& p, const uint16_t* __restrict__ src, int r, int h, int p0,
+                                      uint16_t* rows, uint16_t* trans) {
+  using S = Shape<D>;
+  for (int c = threadIdx.x; c < kStep * S::CHUNKS; c += kThreads) {
+    const int pr = c / S::CHUNKS;
+    const int ch = c % S::CHUNKS;
+    const int pos = p0 + pr;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (pos < p.N) val = *reinterpret_cast<const u32x4*>(src + elem_offset(p, r, pos, h) + ch * 8);
+    if (rows) *reinterpret_cast<u32x4*>(&rows[pr * S::ROW + ch * 8]) = val;
+    if (trans) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        trans[(ch * 8 + 2 * i) * S::TROW + pr] = static_cast<uint16_t>(val[i] & 0xffffu);
+        trans[(ch * 8 + 2 * i + 1) * S::TROW + pr] = static_cast<uint16_t>(val[i] >> 16);
+      }
+    }
+  }
+}
+
+// A operand (rows = 32 positions starting at pos0, k = d) from a staged [pos][d] array.
+template <int D>
+__device__ __forceinline__ u32x4 rows_operand(const uint16_t* rows, int pos0, int ks, int col, int half) {
+  if (D < 16 && half == 1) return u32x4{0u, 0u, 0u, 0u};
+  return *reinterpret_cast<const u32x4*>(&rows[(pos0 + col) * Shape<D>::ROW + ks * 16 + 8 * half]);
+}
+
+// A operand (rows = d, k = 16 positions p0 + 16 t + permutation) from a staged [d][pos]
+// array; the permutation matches the accumulator layout of the tile whose
+// registers 8t..8t+7 become the matching B operand.
+template <int D>
+__device__ __forceinline__ u32x4 trans_operand(const uint16_t* trans, int db, int p0, int t, int col, int half) {
+  const uint16_t* row = &trans[(db * 32 + col) * Shape<D>::TROW];
+  const int b = p0 + 16 * t + 4 * half;
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(row + b);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(row + b + 8);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// B operand from global memory: position pos (lane's column), d = 16 ks + 8 half + i.
+template <int D>
+__device__ __forceinline__ u32x4 global_operand(const Problem& p, const uint16_t* src, int r, int pos, int h, int ks,
+                                                int half) {
+  const int d0 = ks * 16 + 8 * half;
+  if (pos >= p.N || d0 >= D) return u32x4{0u, 0u, 0u, 0u};
+  return *reinterpret_cast<const u32x4*>(src + elem_offset(p, r, pos, h) + d0);
+}
+
+__device__ __forceinline__ f32x16 load_acc_rows(const float* base, int half) {
+  // 16 accumulator registers of a 32-row tile: rows 8g + 4 half + (0..3).
+  f32x16 c;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(base + 8 * g + 4 * half);
+    c[4 * g + 0] = x[0];
+    c[4 * g + 1] = x[1];
+    c[4 * g + 2] = x[2];
+    c[4 * g + 3] = x[3];
+  }
+  return c;
+}
+
+// Store a transposed [d][pos] accumulator (lane = position) as bf16 rows of dst at pos.
+template <int D>
+__device__ __forceinline__ void store_dT(uint16_t* dst_row, const f32x16* acc, float scale, int half) {
+  constexpr int DB = Shape<D>::DB;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + 8 * g + 4 * half;
+      if (d < D) {
+        const u32x2 w = {pack_bf16(acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale),
+                         pack_bf16(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
+        *reinterpret_cast<u32x2*>(dst_row + d) = w;
+      }
+    }
+  }
+}
+
+// Per-query statistics for a step of queries: -lse in log2 units (-inf makes P = 0
+// for padded queries and rows whose keys are all masked) and -D.
+__device__ __forceinline__ void stage_stats(const Problem& p, const BwdArgs& a, int r, int h, int q0, float* nlse,
+                                            float* ndel) {
+  const int t = threadIdx.x;
+  if (t < kStep) {
+    const int j = q0 + t;
+    float nl = -INFINITY, nd = 0.f;
+    if (j < p.N) {
+      const int64_t id = (static_cast<int64_t>(r) * p.H + h) * p.N + j;
+      const float l = a.lse[id];
+      if (l != -INFINITY) nl = -l * kLog2e;
+      nd = -a.delta[id];
+    }
+    nlse[t] = nl;
+    ndel[t] = nd;
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_t,
+                                                               int np) {
+  using S = Shape<D>;
+  __shared__ __align__(16) uint16_t q_rows[kStep * S::ROW];
+  __shared__ __align__(16) uint16_t q_trans[S::DB * 32 * S::TROW];
+  __shared__ __align__(16) uint16_t do_rows[kStep * S::ROW];
+  __shared__ __align__(16) uint16_t do_trans[S::DB * 32 * S::TROW];
+  __shared__ __align__(16) float nlse_lds[kStep];
+  __shared__ __align__(16) float ndel_lds[kStep];
+
+  const int nkb = (p.N + 127) / 128;
+  int blk = blockIdx.x;
+  const int kb = blk % nkb;
+  blk /= nkb;
+  const int h = blk % p.H;
+  const int r = blk / p.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int key = kb * 128 + wave * 32 + col;
+
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* v = static_cast<const uint16_t*>(a.v);
+  const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+  const float sd = sqrtf(static_cast<float>(D));
+  const float c1 = kLog2e / sd;
+
+  u32x4 kreg[S::KS], vreg[S::KS];
+#pragma unroll
+  for (int ks = 0; ks < S::KS; ++ks) {
+    kreg[ks] = global_operand<D>(p, k, r, key, h, ks, half);
+    vreg[ks] = global_operand<D>(p, v, r, key, h, ks, half);
+  }
+  const bool valid = key < p.N;
+  const float mk = (a.mask && valid) ? a.mask[static_cast<int64_t>(r) * p.N + key] : 0.f;
+  const bool wave_live = __ballot(valid && mk != -INFINITY) != 0;
+  const bool any_mask = __ballot(valid && mk != 0.f) != 0;
+  const float mk_s = sd * mk;
+
+  f32x16 dv_acc[S::DB], dk_acc[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dv_acc[db][i] = dk_acc[db][i] = 0.f;
+
+  const float* brow = bias_t + (static_cast<int64_t>(h) * np + key) * np;  // bias^T row of this key
+
+  for (int q0 = 0; q0 < p.N; q0 += kStep) {
+    __syncthreads();
+    stage<D>(p, q, r, h, q0, q_rows, q_trans);
+    stage<D>(p, dout, r, h, q0, do_rows, do_trans);
+    stage_stats(p, a, r, h, q0, nlse_lds, ndel_lds);
+    __syncthreads();
+    if (!wave_live) continue;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      // S = Q K^T + sqrt(d) (bias + mask): rows = queries q0 + 32 qt + ..., lane = key.
+      f32x16 s = load_acc_rows(brow + q0 + 32 * qt, half);
+      if (any_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] += mk_s;
+      }
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) s = mma(rows_operand<D>(q_rows, 32 * qt, ks, col, half), kreg[ks], s);
+      const f32x16 nl = load_acc_rows(nlse_lds + 32 * qt, half);
+      // dP - D = dO V^T - D.
+      f32x16 dp = load_acc_rows(ndel_lds + 32 * qt, half);
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(do_rows, 32 * qt, ks, col, half), vreg[ks], dp);
+      u32x4 pb[2], dsb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pv[i] = fast_exp2(__builtin_fmaf(s[8 * t + i], c1, nl[8 * t + i]));
+          dsv[i] = pv[i] * dp[8 * t + i];
+        }
+        pb[t] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                      pack_bf16(pv[6], pv[7])};
+        dsb[t] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                       pack_bf16(dsv[6], dsv[7])};
+      }
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          dv_acc[db] = mma(trans_operand<D>(do_trans, db, 32 * qt, t, col, half), pb[t], dv_acc[db]);
+          dk_acc[db] = mma(trans_operand<D>(q_trans, db, 32 * qt, t, col, half), dsb[t], dk_acc[db]);
+        }
+      }
+    }
+  }
+  if (!valid) return;
+  const int64_t off = elem_offset(p, r, key, h);
+  store_dT<D>(static_cast<uint16_t*>(a.dv) + off, dv_acc, 1.f, half);
+  store_dT<D>(static_cast<uint16_t*>(a.dk) + off, dk_acc, 1.f / sd, half);
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_f,
+                                                             int np) {
+  using S = Shape<D>;
+  __shared__ __align__(16) uint16_t k_rows[kStep * S::ROW];
+  __shared__ __align__(16) uint16_t k_trans[S::DB * 32 * S::TROW];
+  __shared__ __align__(16) uint16_t v_rows[kStep * S::ROW];
+  __shared__ __align__(16) float m_lds[kStep];
+  __shared__ __align__(16) float ndel4[4][32][4];  // -D of each wave's queries, replicated 4x
+
+  const int nqb = (p.N + 127) / 128;
+  int blk = blockIdx.x;
+  const int qb = blk % nqb;
+  blk /= nqb;
+  const int h = blk % p.H;
+  const int r = blk / p.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int j0 = qb * 128 + wave * 32;
+  const int j = j0 + col;
+  const bool wave_active = j0 < p.N;
+
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* v = static_cast<const uint16_t*>(a.v);
+  const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+  const float sd = sqrtf(static_cast<float>(D));
+  const float c1 = kLog2e / sd;
+
+  u32x4 qreg[S::KS], doreg[S::KS];
+#pragma unroll
+  for (int ks = 0; ks < S::KS; ++ks) {
+    qreg[ks] = global_operand<D>(p, q, r, j, h, ks, half);
+    doreg[ks] = global_operand<D>(p, dout, r, j, h, ks, half);
+  }
+  float nl = -INFINITY, nd = 0.f;
+  if (j < p.N) {
+    const int64_t id = (static_cast<int64_t>(r) * p.H + h) * p.N + j;
+    const float l = a.lse[id];
+    if (l != -INFINITY) nl = -l * kLog2e;
+    nd = -a.delta[id];
+  }
+  if (half == 0) {
+    *reinterpret_cast<f32x4*>(&ndel4[wave][col][0]) = f32x4{nd, nd, nd, nd};
+  }
+  const bool row_live = __ballot(nl != -INFINITY) != 0;
+
+  f32x16 dq_acc[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq_acc[db][i] = 0.f;
+
+  const float* brow = bias_f + (static_cast<int64_t>(h) * np + j) * np;
+  const float* mrow = a.mask ? a.mask + static_cast<int64_t>(r) * p.N : nullptr;
+
+  for (int k0 = 0; k0 < p.N; k0 += kStep) {
+    const int kk = k0 + lane;
+    const bool kvalid = kk < p.N;
+    const float mv = (mrow && kvalid) ? mrow[kk] : 0.f;
+    if (__ballot(kvalid && mv != -INFINITY) == 0) continue;
+    const bool any_mask = __ballot(kvalid && mv != 0.f) != 0;
+    __syncthreads();
+    stage<D>(p, k, r, h, k0, k_rows, k_trans);
+    stage<D>(p, v, r, h, k0, v_rows, nullptr);
+    if (any_mask && tid < kStep) m_lds[tid] = kvalid ? sd * mv : -INFINITY;
+    __syncthreads();
+    if (!wave_active || !row_live) continue;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      // S^T = K Q^T + sqrt(d) (bias + mask): rows = keys k0 + 32 mb + ..., lane = query.
+      f32x16 s = load_acc_rows(brow + k0 + 32 * mb, half);
+      if (any_mask) {
+        const f32x16 mm = load_acc_rows(m_lds + 32 * mb, half);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] += mm[i];
+      }
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) s = mma(rows_operand<D>(k_rows, 32 * mb, ks, col, half), qreg[ks], s);
+      // dP^T - D = V dO^T - D (accumulator starts at -D of the lane's query).
+      f32x16 dp;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&ndel4[wave][col][0]);
+        dp[4 * g + 0] = x[0];
+        dp[4 * g + 1] = x[1];
+        dp[4 * g + 2] = x[2];
+        dp[4 * g + 3] = x[3];
+      }
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(v_rows, 32 * mb, ks, col, half), doreg[ks], dp);
+      u32x4 dsb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float dsv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsv[i] = fast_exp2(__builtin_fmaf(s[8 * t + i], c1, nl)) * dp[8 * t + i];
+        dsb[t] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                       pack_bf16(dsv[6], dsv[7])};
+      }
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) dq_acc[db] = mma(trans_operand<D>(k_trans, db, 32 * mb, t, col, half), dsb[t], dq_acc[db]);
+    }
+  }
+  if (!wave_active || j >= p.N) return;
+  store_dT<D>(static_cast<uint16_t*>(a.dq) + elem_offset(p, r, j, h), dq_acc, 1.f / sd, half);
+}
+
+// ------------------------------------------------------------------ dBias
+// Workgroup = (head, 64-query block, 128-key block, row group); wave w owns keys
+// 32w..32w+31 of the block and both 32-query tiles.  Rows of the group are
+// visited in increasing order and dS is summed in registers.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dbias_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_t,
+                                                                int np, int row_groups, float* __restrict__ out) {
+  using S = Shape<D>;
+  __shared__ __align__(16) uint16_t q_rows[kStep * S::ROW];
+  __shared__ __align__(16) uint16_t do_rows[kStep * S::ROW];
+  __shared__ __align__(16) float nlse_lds[kStep];
+  __shared__ __align__(16) float ndel_lds[kStep];
+
+  const int nkb = (p.N + 127) / 128;
+  const int nqb = (p.N + kStep - 1) / kStep;
+  int blk = blockIdx.x;
+  const int kb = blk % nkb;
+  blk /= nkb;
+  const int qb = blk % nqb;
+  blk /= nqb;
+  const int h = blk % p.H;
+  const int g = blk / p.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int key = kb * 128 + wave * 32 + col;
+  const int q0 = qb * kStep;
+  const bool valid = key < p.N;
+
+  const int rows_per = (p.R + row_groups - 1) / row_groups;
+  const int r_begin = g * rows_per;
+  const int r_end = min(p.R, r_begin + rows_per);
+
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* v = static_cast<const uint16_t*>(a.v);
+  const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+  const float sd = sqrtf(static_cast<float>(D));
+  const float c1 = kLog2e / sd;
+
+  const float* brow = bias_t + (static_cast<int64_t>(h) * np + key) * np + q0;
+  const f32x16 b0 = load_acc_rows(brow, half);
+  const f32x16 b1 = load_acc_rows(brow + 32, half);
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
+
+  for (int r = r_begin; r < r_end; ++r) {
+    const float mk = (a.mask && valid) ? a.mask[static_cast<int64_t>(r) * p.N + key] : 0.f;
+    const bool wave_live = __ballot(valid && mk != -INFINITY) != 0;
+    const bool any_mask = __ballot(valid && mk != 0.f) != 0;
+    __syncthreads();
+    stage<D>(p, q, r, h, q0, q_rows, nullptr);
+    stage<D>(p, dout, r, h, q0, do_rows, nullptr);
+    stage_stats(p, a, r, h, q0, nlse_lds, ndel_lds);
+    u32x4 kreg[S::KS], vreg[S::KS];
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      kreg[ks] = global_operand<D>(p, k, r, key, h, ks, half);
+      vreg[ks] = global_operand<D>(p, v, r, key, h, ks, half);
+    }
+    __syncthreads();
+    if (!wave_live) continue;
+    const float mk_s = sd * mk;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      f32x16 s = qt == 0 ? b0 : b1;
+      if (any_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] += mk_s;
+      }
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) s = mma(rows_operand<D>(q_rows, 32 * qt, ks, col, half), kreg[ks], s);
+      const f32x16 nl = load_acc_rows(nlse_lds + 32 * qt, half);
+      f32x16 dp = load_acc_rows(ndel_lds + 32 * qt, half);
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(do_rows, 32 * qt, ks, col, half), vreg[ks], dp);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[qt][i] += fast_exp2(__builtin_fmaf(s[i], c1, nl[i])) * dp[i];
+    }
+  }
+  if (!valid) return;
+  float* dst = out + static_cast<int64_t>(g) * p.H * p.N * p.N + static_cast<int64_t>(h) * p.N * p.N + key;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int jq = q0 + 32 * qt + acc_row(i, lane);
+      if (jq < p.N) dst[static_cast<int64_t>(jq) * p.N] = acc[qt][i];
+    }
+}
+
+// dbias[i] = sum over groups g = 0, 1, ... of part[g][i], in increasing g.
+__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restrict__ part, int groups, int64_t n,
+                                                           float* __restrict__ dbias) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float s = part[i];
+    for (int g = 1; g < groups; ++g) s += part[static_cast<int64_t>(g) * n + i];
+    dbias[i] = s;
+  }
+}
+
+// delta[r,h,j] = sum_c dout[r,j,h,c] * o[r,j,h,c]; one lane per softmax row.
+template <int D>
+__global__ __launch_bounds__(256) void delta_bf16_kernel(Problem p, BwdArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(p.R) * p.H * p.N;
+  if (idx >= total) return;
+  const int j = static_cast<int>(idx % p.N);
+  const int h = static_cast<int>((idx / p.N) % p.H);
+  const int r = static_cast<int>(idx / (static_cast<int64_t>(p.N) * p.H));
+  const int64_t off = elem_offset(p, r, j, h);
+  const u32x4* o = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.o) + off);
+  const u32x4* d = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dout) + off);
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4 x = o[c], y = d[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s += __uint_as_float(x[i] << 16) * __uint_as_float(y[i] << 16);
+      s += __uint_as_float(x[i] & 0xffff0000u) * __uint_as_float(y[i] & 0xffff0000u);
+    }
+  }
+  a.delta[idx] = s;
+}
+
+int dbias_row_groups(const Problem& p) {
+  const int64_t tiles = static_cast<int64_t>(p.H) * ((p.N + kStep - 1) / kStep) * ((p.N + 127) / 128);
+  int64_t g = (2048 + tiles - 1) / tiles;  // aim for >= 2048 workgroups
+  g = std::max<int64_t>(1, std::min<int64_t>(g, std::min<int64_t>(16, p.R)));
+  return static_cast<int>(g);
+}
+
+template <int D>
+hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_f, float* bias_t, int np,
+                             float* dbias_part, int groups, hipStream_t s) {
+  hipError_t e;
+  {
+    const int64_t rows_total = static_cast<int64_t>(p.R) * p.H * p.N;
+    KernelTimer timer("bwd_delta", s);
+    hipLaunchKernelGGL((delta_bf16_kernel<D>), dim3(static_cast<unsigned>((rows_total + 255) / 256)), dim3(256), 0,
+                       s, p, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = launch_bias_prep(p, a.bias, bias_t, np, 1, s)) != hipSuccess) return e;
+  if ((e = launch_bias_prep(p, a.bias, bias_f, np, 0, s)) != hipSuccess) return e;
+  {
+    const int64_t blocks = static_cast<int64_t>((p.N + 127) / 128) * p.H * p.R;
+    KernelTimer timer("bwd_dkdv_mfma", s);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p, a, bias_t,
+                       np);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    const int64_t blocks = static_cast<int64_t>((p.N + 127) / 128) * p.H * p.R;
+    KernelTimer timer("bwd_dq_mfma", s);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p, a, bias_f,
+                       np);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.dbias) {
+    const int64_t blocks =
+        static_cast<int64_t>((p.N + 127) / 128) * ((p.N + kStep - 1) / kStep) * p.H * groups;
+    float* target = groups == 1 ? a.dbias : dbias_part;
+    {
+      KernelTimer timer("bwd_dbias_mfma", s);
+      hipLaunchKernelGGL((bwd_dbias_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p, a,
+                         bias_t, np, groups, target);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (groups > 1) {
+      const int64_t n = static_cast<int64_t>(p.H) * p.N * p.N;
+      const int rb = static_cast<int>(std::min<int64_t>((n + 255) / 256, 4096));
+      KernelTimer timer("bwd_dbias_reduce", s);
+      hipLaunchKernelGGL(dbias_reduce_kernel, dim3(rb), dim3(256), 0, s, dbias_part, groups, n, a.dbias);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+// Workspace: delta [R,H,N] | bias_f [H,np,np] | bias_t [H,np,np] | dbias partials [G,H,N,N].
+size_t bwd_mfma_workspace_bytes(const Problem& p) {
+  const size_t np = static_cast<size_t>(bias_pad(p.N));
+  const int groups = dbias_row_groups(p);
+  const size_t delta = align_up(static_cast<size_t>(p.R) * p.H * p.N * sizeof(float));
+  const size_t bias = align_up(static_cast<size_t>(p.H) * np * np * sizeof(float));
+  const size_t part = groups > 1 ? align_up(static_cast<size_t>(groups) * p.H * p.N * p.N * sizeof(float)) : 0;
+  return delta + 2 * bias + part;
+}
+
+hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& args, void* ws, hipStream_t s) {
+  const size_t np = static_cast<size_t>(bias_pad(p.N));
+  const int groups = dbias_row_groups(p);
+  char* base = static_cast<char*>(ws);
+  BwdArgs a = args;
+  a.delta = reinterpret_cast<float*>(base);
+  base += align_up(static_cast<size_t>(p.R) * p.H * p.N * sizeof(float));
+  float* bias_f = reinterpret_cast<float*>(base);
+  base += align_up(static_cast<size_t>(p.H) * np * np * sizeof(float));
+  float* bias_t = reinterpret_cast<float*>(base);
+  base += align_up(static_cast<size_t>(p.H) * np * np * sizeof(float));
+  float* part = reinterpret_cast<float*>(base);
+  switch (p.D) {
+    case 8: return bwd_mfma_dispatch<8>(p, a, bias_f, bias_t, static_cast<int>(np), part, groups, s);
+    case 16: return bwd_mfma_dispatch<16>(p, a, bias_f, bias_t, static_cast<int>(np), part, groups, s);
+    case 32: return bwd_mfma_dispatch<32>(p, a, bias_f, bias_t, static_cast<int>(np), part, groups, s);
+    case 64: return bwd_mfma_dispatch<64>(p, a, bias_f, bias_t, static_cast<int>(np), part, groups, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace evo

@@ -41,6 +41,7 @@ KERNEL_FLOP_FACTOR = {
     "bwd_mfma": (10.0, "mfma"),
     "bwd_dkdv_mfma": (8.0, "mfma"),
     "bwd_dq_mfma": (6.0, "mfma"),
+    "bwd_dbias_mfma": (4.0, "mfma"),
     "fwd_vector": (4.0, "alu"),
     "bwd_dq_vector": (6.0, "alu"),
     "bwd_dkdv_vector": (8.0, "alu"),

@@ -32,132 +32,40 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kThreads = 256;
-constexpr int kStep = 64;  // queries (dkdv, dbias) or keys (dq) staged per step
-
-template <int D>
-struct Shape {
-  static constexpr int KS = D >= 16 ? D / 16 : 1;  // 16-deep steps over d
-  static constexpr int DB = D >= 32 ? D / 32 : 1;  // 32-row blocks over d for transposed outputs
-  static constexpr int ROW = KS * 16 + 8;          // bf16 per staged [pos][d] row (8 padding)
-  static constexpr int TROW = kStep + 8;           // bf16 per staged [d][pos] row (8 padding)
-  static constexpr int CHUNKS = D / 8;             // 16-byte chunks per position
-};
-
-// Stage kStep positions starting at p0 of one (row, head) of `src` into LDS:
-// row-major [pos][d] (if rows != nullptr) and transposed [d][pos] (if trans != nullptr).
-// Positions >= N are zero.
-template <int D>
-__device__ __forceinline__ void stage(const Problem& p, const uint16_t* __restrict__ src, int r, int h, int p0,
-                                      uint16_t* rows, uint16_t* trans) {
-  using S = Shape<D>;
-  for (int c = threadIdx.x; c < kStep * S::CHUNKS; c += kThreads) {
-    const int pr = c / S::CHUNKS;
-    const int ch = c % S::CHUNKS;
-    const int pos = p0 + pr;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (pos < p.N) val = *reinterpret_cast<const u32x4*>(src + elem_offset(p, r, pos, h) + ch * 8);
-    if (rows) *reinterpret_cast<u32x4*>(&rows[pr * S::ROW + ch * 8]) = val;
-    if (trans) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        trans[(ch * 8 + 2 * i) * S::TROW + pr] = static_cast<uint16_t>(val[i] & 0xffffu);
-        trans[(ch * 8 + 2 * i + 1) * S::TROW + pr] = static_cast<uint16_t>(val[i] >> 16);
-      }
-    }
-  }
-}
-
-// A operand (rows = 32 positions starting at pos0, k = d) from a staged [pos][d] array.
-template <int D>
-__device__ __forceinline__ u32x4 rows_operand(const uint16_t* rows, int pos0, int ks, int col, int half) {
-  if (D < 16 && half == 1) return u32x4{0u, 0u, 0u, 0u};
-  return *reinterpret_cast<const u32x4*>(&rows[(pos0 + col) * Shape<D>::ROW + ks * 16 + 8 * half]);
-}
-
-// A operand (rows = d, k = 16 positions p0 + 16 t + permutation) from a staged [d][pos]
-// array; the permutation matches the accumulator layout of the tile whose
-// registers 8t..8t+7 become the matching B operand.
-template <int D>
-__device__ __forceinline__ u32x4 trans_operand(const uint16_t* trans, int db, int p0, int t, int col, int half) {
-  const uint16_t* row = &trans[(db * 32 + col) * Shape<D>::TROW];
-  const int b = p0 + 16 * t + 4 * half;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(row + b);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(row + b + 8);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-
-// B operand from global memory: position pos (lane's column), d = 16 ks + 8 half + i.
-template <int D>
-__device__ __forceinline__ u32x4 global_operand(const Problem& p, const uint16_t* src, int r, int pos, int h, int ks,
-                                                int half) {
-  const int d0 = ks * 16 + 8 * half;
-  if (pos >= p.N || d0 >= D) return u32x4{0u, 0u, 0u, 0u};
-  return *reinterpret_cast<const u32x4*>(src + elem_offset(p, r, pos, h) + d0);
-}
-
-__device__ __forceinline__ f32x16 load_acc_rows(const float* base, int half) {
-  // 16 accumulator registers of a 32-row tile: rows 8g + 4 half + (0..3).
-  f32x16 c;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(base + 8 * g + 4 * half);
-    c[4 * g + 0] = x[0];
-    c[4 * g + 1] = x[1];
-    c[4 * g + 2] = x[2];
-    c[4 * g + 3] = x[3];
-  }
-  return c;
-}
-
-// Store a transposed [d][pos] accumulator (lane = position) as bf16 rows of dst at pos.
-template <int D>
-__device__ __forceinline__ void store_dT(uint16_t* dst_row, const f32x16* acc, float scale, int half) {
-  constexpr int DB = Shape<D>::DB;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = db * 32 + 8 * g + 4 * half;
-      if (d < D) {
-        const u32x2 w = {pack_bf16(acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale),
-                         pack_bf16(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
-        *reinterpret_cast<u32x2*>(dst_row + d) = w;
-      }
-    }
-  }
-}
-
-// Per-query statistics for a step of queries: -lse in log2 units (-inf makes P = 0
-// for padded queries and rows whose keys are all masked) and -D.
-__device__ __forceinline__ void stage_stats(const Problem& p, const BwdArgs& a, int r, int h, int q0, float* nlse,
-                                            float* ndel) {
-  const int t = threadIdx.x;
-  if (t < kStep) {
-    const int j = q0 + t;
-    float nl = -INFINITY, nd = 0.f;
-    if (j < p.N) {
+// Per-query statistics of a step of queries: -lse in log2 units (-inf gives
+// P = 0 for padded queries and for rows whose keys are all masked) and -D.
+struct StatStage {
+  float nl, nd;
+  __device__ __forceinline__ void load(const Problem& p, const BwdArgs& a, int r, int h, int q0) {
+    nl = -INFINITY;
+    nd = 0.f;
+    const int j = q0 + static_cast<int>(threadIdx.x);
+    if (threadIdx.x < kStep && j < p.N) {
       const int64_t id = (static_cast<int64_t>(r) * p.H + h) * p.N + j;
       const float l = a.lse[id];
       if (l != -INFINITY) nl = -l * kLog2e;
       nd = -a.delta[id];
     }
-    nlse[t] = nl;
-    ndel[t] = nd;
   }
-}
+  __device__ __forceinline__ void store(float* nlse, float* ndel) const {
+    if (threadIdx.x < kStep) {
+      nlse[threadIdx.x] = nl;
+      ndel[threadIdx.x] = nd;
+    }
+  }
+};
 
 // ------------------------------------------------------------------ dK, dV
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_t,
                                                                int np) {
   using S = Shape<D>;
-  __shared__ __align__(16) uint16_t q_rows[kStep * S::ROW];
-  __shared__ __align__(16) uint16_t q_trans[S::DB * 32 * S::TROW];
-  __shared__ __align__(16) uint16_t do_rows[kStep * S::ROW];
-  __shared__ __align__(16) uint16_t do_trans[S::DB * 32 * S::TROW];
-  __shared__ __align__(16) float nlse_lds[kStep];
-  __shared__ __align__(16) float ndel_lds[kStep];
+  __shared__ __align__(16) uint16_t q_rows[2][kStep * S::ROW];
+  __shared__ __align__(16) uint16_t q_trans[2][S::DB * 32 * S::TROW];
+  __shared__ __align__(16) uint16_t do_rows[2][kStep * S::ROW];
+  __shared__ __align__(16) uint16_t do_trans[2][S::DB * 32 * S::TROW];
+  __shared__ __align__(16) float nlse_lds[2][kStep];
+  __shared__ __align__(16) float ndel_lds[2][kStep];
 
   const int nkb = (p.N + 127) / 128;
   int blk = blockIdx.x;
@@ -166,7 +74,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(Problem p, BwdArg
   const int h = blk % p.H;
   const int r = blk / p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int key = kb * 128 + wave * 32 + col;
+  const int key = kb * 128 + wave * 32 + col;  // < np
 
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* k = static_cast<const uint16_t*>(a.k);
@@ -195,35 +103,68 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(Problem p, BwdArg
 
   const float* brow = bias_t + (static_cast<int64_t>(h) * np + key) * np;  // bias^T row of this key
 
+  const int64_t rh = row_head_offset(p, r, h);
+  const int64_t pstep = pos_step(p);
+  const uint16_t* qbase = q + rh;
+  const uint16_t* dobase = dout + rh;
+  Stage<D> qst, dost;
+  qst.init(p);
+  dost.init(p);
+  StatStage stst;
+  f32x16 bnext[2];
+  qst.load(qbase, 0, p.N);
+  dost.load(dobase, 0, p.N);
+  stst.load(p, a, r, h, 0);
+  if (wave_live) {
+    bnext[0] = load_acc_rows(brow, half);
+    bnext[1] = load_acc_rows(brow + 32, half);
+  }
+
+  int buf = 0;
   for (int q0 = 0; q0 < p.N; q0 += kStep) {
-    __syncthreads();
-    stage<D>(p, q, r, h, q0, q_rows, q_trans);
-    stage<D>(p, dout, r, h, q0, do_rows, do_trans);
-    stage_stats(p, a, r, h, q0, nlse_lds, ndel_lds);
-    __syncthreads();
+    qst.store(q_rows[buf], q_trans[buf], S::ROW, q0, p.N);
+    dost.store(do_rows[buf], do_trans[buf], S::ROW, q0, p.N);
+    stst.store(nlse_lds[buf], ndel_lds[buf]);
+    lds_barrier();
+    const int cb = buf;
+    buf ^= 1;
+    // S = Q K^T + sqrt(d) (bias + mask): rows = queries q0 + 32 qt + ..., lane = key.
+    f32x16 s[2];
+    if (wave_live) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        f32x16 c = bnext[qt];
+        if (any_mask) c += mk_s;
+        s[qt] = mma(rows_operand<D>(q_rows[cb], 32 * qt, 0, col, half), kreg[0], c);
+#pragma unroll
+        for (int ks = 1; ks < S::KS; ++ks) s[qt] = mma(rows_operand<D>(q_rows[cb], 32 * qt, ks, col, half), kreg[ks], s[qt]);
+      }
+    }
+    const int q1 = q0 + kStep;
+    if (q1 < p.N) {
+      qst.load(qbase + q1 * pstep, q1, p.N);
+      dost.load(dobase + q1 * pstep, q1, p.N);
+      stst.load(p, a, r, h, q1);
+      if (wave_live) {
+        bnext[0] = load_acc_rows(brow + q1, half);
+        bnext[1] = load_acc_rows(brow + q1 + 32, half);
+      }
+    }
     if (!wave_live) continue;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      // S = Q K^T + sqrt(d) (bias + mask): rows = queries q0 + 32 qt + ..., lane = key.
-      f32x16 s = load_acc_rows(brow + q0 + 32 * qt, half);
-      if (any_mask) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] += mk_s;
-      }
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) s = mma(rows_operand<D>(q_rows, 32 * qt, ks, col, half), kreg[ks], s);
-      const f32x16 nl = load_acc_rows(nlse_lds + 32 * qt, half);
+      const f32x16 nl = load_acc_rows(&nlse_lds[cb][32 * qt], half);
       // dP - D = dO V^T - D.
-      f32x16 dp = load_acc_rows(ndel_lds + 32 * qt, half);
+      f32x16 dp = load_acc_rows(&ndel_lds[cb][32 * qt], half);
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(do_rows, 32 * qt, ks, col, half), vreg[ks], dp);
+      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(do_rows[cb], 32 * qt, ks, col, half), vreg[ks], dp);
       u32x4 pb[2], dsb[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         float pv[8], dsv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          pv[i] = fast_exp2(__builtin_fmaf(s[8 * t + i], c1, nl[8 * t + i]));
+          pv[i] = fast_exp2(__builtin_fmaf(s[qt][8 * t + i], c1, nl[8 * t + i]));
           dsv[i] = pv[i] * dp[8 * t + i];
         }
         pb[t] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
@@ -235,8 +176,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(Problem p, BwdArg
       for (int db = 0; db < S::DB; ++db) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          dv_acc[db] = mma(trans_operand<D>(do_trans, db, 32 * qt, t, col, half), pb[t], dv_acc[db]);
-          dk_acc[db] = mma(trans_operand<D>(q_trans, db, 32 * qt, t, col, half), dsb[t], dk_acc[db]);
+          dv_acc[db] = mma(trans_operand<D>(do_trans[cb], db, 32 * qt, t, col, half), pb[t], dv_acc[db]);
+          dk_acc[db] = mma(trans_operand<D>(q_trans[cb], db, 32 * qt, t, col, half), dsb[t], dk_acc[db]);
         }
       }
     }
@@ -252,10 +193,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_f,
                                                              int np) {
   using S = Shape<D>;
-  __shared__ __align__(16) uint16_t k_rows[kStep * S::ROW];
-  __shared__ __align__(16) uint16_t k_trans[S::DB * 32 * S::TROW];
-  __shared__ __align__(16) uint16_t v_rows[kStep * S::ROW];
-  __shared__ __align__(16) float m_lds[kStep];
+  __shared__ __align__(16) uint16_t k_rows[2][kStep * S::ROW];
+  __shared__ __align__(16) uint16_t k_trans[2][S::DB * 32 * S::TROW];
+  __shared__ __align__(16) uint16_t v_rows[2][kStep * S::ROW];
+  __shared__ __align__(16) float m_lds[2][kStep];
   __shared__ __align__(16) float ndel4[4][32][4];  // -D of each wave's queries, replicated 4x
 
   const int nqb = (p.N + 127) / 128;
@@ -266,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Problem p, BwdArgs 
   const int r = blk / p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int j0 = qb * 128 + wave * 32;
-  const int j = j0 + col;
+  const int j = j0 + col;  // < np
   const bool wave_active = j0 < p.N;
 
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
@@ -289,10 +230,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Problem p, BwdArgs 
     if (l != -INFINITY) nl = -l * kLog2e;
     nd = -a.delta[id];
   }
-  if (half == 0) {
-    *reinterpret_cast<f32x4*>(&ndel4[wave][col][0]) = f32x4{nd, nd, nd, nd};
-  }
-  const bool row_live = __ballot(nl != -INFINITY) != 0;
+  if (half == 0) *reinterpret_cast<f32x4*>(&ndel4[wave][col][0]) = f32x4{nd, nd, nd, nd};
+  const bool row_live = wave_active && __ballot(nl != -INFINITY) != 0;
 
   f32x16 dq_acc[S::DB];
 #pragma unroll
@@ -300,33 +239,68 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Problem p, BwdArgs 
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq_acc[db][i] = 0.f;
 
-  const float* brow = bias_f + (static_cast<int64_t>(h) * np + j) * np;
   const float* mrow = a.mask ? a.mask + static_cast<int64_t>(r) * p.N : nullptr;
 
+  const int64_t rh = row_head_offset(p, r, h);
+  const int64_t pstep = pos_step(p);
+  const uint16_t* kbase = k + rh;
+  const uint16_t* vbase = v + rh;
+  const float* bhead = bias_f + static_cast<int64_t>(h) * np * np;
+  const uint32_t boff = static_cast<uint32_t>(j * np);
+  Stage<D> kst, vst;
+  kst.init(p);
+  vst.init(p);
+  f32x16 bnext[2];
+  float mnext = 0.f;
+  kst.load(kbase, 0, p.N);
+  vst.load(vbase, 0, p.N);
+  if (mrow) mnext = mrow[min(lane, p.N - 1)];
+  if (row_live) {
+    bnext[0] = load_acc_rows(bhead + boff, half);
+    bnext[1] = load_acc_rows(bhead + boff + 32, half);
+  }
+
+  int buf = 0;
   for (int k0 = 0; k0 < p.N; k0 += kStep) {
-    const int kk = k0 + lane;
-    const bool kvalid = kk < p.N;
-    const float mv = (mrow && kvalid) ? mrow[kk] : 0.f;
-    if (__ballot(kvalid && mv != -INFINITY) == 0) continue;
+    const bool kvalid = k0 + lane < p.N;
+    const float mv = kvalid ? mnext : 0.f;
+    const bool live = __ballot(kvalid && mv != -INFINITY) != 0;
     const bool any_mask = __ballot(kvalid && mv != 0.f) != 0;
-    __syncthreads();
-    stage<D>(p, k, r, h, k0, k_rows, k_trans);
-    stage<D>(p, v, r, h, k0, v_rows, nullptr);
-    if (any_mask && tid < kStep) m_lds[tid] = kvalid ? sd * mv : -INFINITY;
-    __syncthreads();
-    if (!wave_active || !row_live) continue;
+    const bool compute = live && row_live;
+    const int cb = buf;
+    if (live) {
+      kst.store(k_rows[buf], k_trans[buf], S::ROW, k0, p.N);
+      vst.store(v_rows[buf], nullptr, S::ROW, k0, p.N);
+      if (any_mask && tid < kStep) m_lds[buf][tid] = kvalid ? sd * mv : -INFINITY;
+      lds_barrier();
+      buf ^= 1;
+    }
+    // S^T = K Q^T + sqrt(d) (bias + mask): rows = keys k0 + 32 mb + ..., lane = query.
+    f32x16 s[2];
+    if (compute) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16 c = bnext[mb];
+        if (any_mask) c += load_acc_rows(&m_lds[cb][32 * mb], half);
+        s[mb] = mma(rows_operand<D>(k_rows[cb], 32 * mb, 0, col, half), qreg[0], c);
+#pragma unroll
+        for (int ks = 1; ks < S::KS; ++ks) s[mb] = mma(rows_operand<D>(k_rows[cb], 32 * mb, ks, col, half), qreg[ks], s[mb]);
+      }
+    }
+    const int k1 = k0 + kStep;
+    if (k1 < p.N) {
+      kst.load(kbase + k1 * pstep, k1, p.N);
+      vst.load(vbase + k1 * pstep, k1, p.N);
+      if (mrow) mnext = mrow[min(k1 + lane, p.N - 1)];
+      if (row_live) {
+        bnext[0] = load_acc_rows(bhead + k1 + boff, half);
+        bnext[1] = load_acc_rows(bhead + k1 + boff + 32, half);
+      }
+    }
+    if (!compute) continue;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      // S^T = K Q^T + sqrt(d) (bias + mask): rows = keys k0 + 32 mb + ..., lane = query.
-      f32x16 s = load_acc_rows(brow + k0 + 32 * mb, half);
-      if (any_mask) {
-        const f32x16 mm = load_acc_rows(m_lds + 32 * mb, half);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] += mm[i];
-      }
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) s = mma(rows_operand<D>(k_rows, 32 * mb, ks, col, half), qreg[ks], s);
-      // dP^T - D = V dO^T - D (accumulator starts at -D of the lane's query).
+      // dP^T - D = V dO^T - D; the accumulator starts at -D of the lane's query.
       f32x16 dp;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -337,20 +311,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Problem p, BwdArgs 
         dp[4 * g + 3] = x[3];
       }
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(v_rows, 32 * mb, ks, col, half), doreg[ks], dp);
+      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(v_rows[cb], 32 * mb, ks, col, half), doreg[ks], dp);
       u32x4 dsb[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         float dsv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dsv[i] = fast_exp2(__builtin_fmaf(s[8 * t + i], c1, nl)) * dp[8 * t + i];
+        for (int i = 0; i < 8; ++i) dsv[i] = fast_exp2(__builtin_fmaf(s[mb][8 * t + i], c1, nl)) * dp[8 * t + i];
         dsb[t] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
                        pack_bf16(dsv[6], dsv[7])};
       }
 #pragma unroll
       for (int db = 0; db < S::DB; ++db)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) dq_acc[db] = mma(trans_operand<D>(k_trans, db, 32 * mb, t, col, half), dsb[t], dq_acc[db]);
+        for (int t = 0; t < 2; ++t)
+          dq_acc[db] = mma(trans_operand<D>(k_trans[cb], db, 32 * mb, t, col, half), dsb[t], dq_acc[db]);
     }
   }
   if (!wave_active || j >= p.N) return;
@@ -365,10 +340,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dbias_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_t,
                                                                 int np, int row_groups, float* __restrict__ out) {
   using S = Shape<D>;
-  __shared__ __align__(16) uint16_t q_rows[kStep * S::ROW];
-  __shared__ __align__(16) uint16_t do_rows[kStep * S::ROW];
-  __shared__ __align__(16) float nlse_lds[kStep];
-  __shared__ __align__(16) float ndel_lds[kStep];
+  __shared__ __align__(16) uint16_t q_rows[2][kStep * S::ROW];
+  __shared__ __align__(16) uint16_t do_rows[2][kStep * S::ROW];
+  __shared__ __align__(16) float nlse_lds[2][kStep];
+  __shared__ __align__(16) float ndel_lds[2][kStep];
 
   const int nkb = (p.N + 127) / 128;
   const int nqb = (p.N + kStep - 1) / kStep;
@@ -380,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dbias_kernel(Problem p, BwdAr
   const int h = blk % p.H;
   const int g = blk / p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int key = kb * 128 + wave * 32 + col;
+  const int key = kb * 128 + wave * 32 + col;  // < np
   const int q0 = qb * kStep;
   const bool valid = key < p.N;
 
@@ -403,36 +378,59 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dbias_kernel(Problem p, BwdAr
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
 
+  const int64_t pstep = pos_step(p);
+  Stage<D> qst, dost;
+  qst.init(p);
+  dost.init(p);
+  StatStage stst;
+  u32x4 knext[S::KS], vnext[S::KS];
+  float mnext = 0.f;
+  // Row r's query block q0 starts at element (r, q0, h, 0).
+  auto fetch = [&](int r) {
+    const int64_t base = row_head_offset(p, r, h) + q0 * pstep;
+    qst.load(q + base, q0, p.N);
+    dost.load(dout + base, q0, p.N);
+    stst.load(p, a, r, h, q0);
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      knext[ks] = global_operand<D>(p, k, r, key, h, ks, half);
+      vnext[ks] = global_operand<D>(p, v, r, key, h, ks, half);
+    }
+    mnext = (a.mask && valid) ? a.mask[static_cast<int64_t>(r) * p.N + key] : 0.f;
+  };
+  if (r_begin < r_end) fetch(r_begin);
+
+  int buf = 0;
   for (int r = r_begin; r < r_end; ++r) {
-    const float mk = (a.mask && valid) ? a.mask[static_cast<int64_t>(r) * p.N + key] : 0.f;
-    const bool wave_live = __ballot(valid && mk != -INFINITY) != 0;
-    const bool any_mask = __ballot(valid && mk != 0.f) != 0;
-    __syncthreads();
-    stage<D>(p, q, r, h, q0, q_rows, nullptr);
-    stage<D>(p, dout, r, h, q0, do_rows, nullptr);
-    stage_stats(p, a, r, h, q0, nlse_lds, ndel_lds);
+    qst.store(q_rows[buf], nullptr, S::ROW, q0, p.N);
+    dost.store(do_rows[buf], nullptr, S::ROW, q0, p.N);
+    stst.store(nlse_lds[buf], ndel_lds[buf]);
     u32x4 kreg[S::KS], vreg[S::KS];
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) {
-      kreg[ks] = global_operand<D>(p, k, r, key, h, ks, half);
-      vreg[ks] = global_operand<D>(p, v, r, key, h, ks, half);
+      kreg[ks] = knext[ks];
+      vreg[ks] = vnext[ks];
     }
-    __syncthreads();
+    const float mk = mnext;
+    lds_barrier();
+    const int cb = buf;
+    buf ^= 1;
+    if (r + 1 < r_end) fetch(r + 1);
+    const bool wave_live = __ballot(valid && mk != -INFINITY) != 0;
     if (!wave_live) continue;
+    const bool any_mask = __ballot(valid && mk != 0.f) != 0;
     const float mk_s = sd * mk;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      f32x16 s = qt == 0 ? b0 : b1;
-      if (any_mask) {
+      f32x16 c = qt == 0 ? b0 : b1;
+      if (any_mask) c += mk_s;
+      f32x16 s = mma(rows_operand<D>(q_rows[cb], 32 * qt, 0, col, half), kreg[0], c);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] += mk_s;
-      }
+      for (int ks = 1; ks < S::KS; ++ks) s = mma(rows_operand<D>(q_rows[cb], 32 * qt, ks, col, half), kreg[ks], s);
+      const f32x16 nl = load_acc_rows(&nlse_lds[cb][32 * qt], half);
+      f32x16 dp = load_acc_rows(&ndel_lds[cb][32 * qt], half);
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) s = mma(rows_operand<D>(q_rows, 32 * qt, ks, col, half), kreg[ks], s);
-      const f32x16 nl = load_acc_rows(nlse_lds + 32 * qt, half);
-      f32x16 dp = load_acc_rows(ndel_lds + 32 * qt, half);
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(do_rows, 32 * qt, ks, col, half), vreg[ks], dp);
+      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(do_rows[cb], 32 * qt, ks, col, half), vreg[ks], dp);
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[qt][i] += fast_exp2(__builtin_fmaf(s[i], c1, nl[i])) * dp[i];
     }

@@ -30,9 +30,10 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kFwdThreads = 256;
-constexpr int kFwdQueries = 128;  // per workgroup
-constexpr int kFwdKeys = 64;      // per step
+constexpr int kFwdQueries = 128;  // queries per workgroup (32 per wave)
+// Attention rows per wave; the rows of a wave share each load of the bias tile.
+template <int D>
+constexpr int fwd_rows() { return D <= 32 ? 2 : 1; }
 
 // out[h][j][k] = sqrt(d) * bias[h][j][k] for j, k < N; -inf for k >= N (padding keys
 // never win the softmax); 0 for padding queries.  Row stride nk, nq rows per head.
@@ -62,199 +63,211 @@ __global__ __launch_bounds__(256) void bias_prep_kernel(Problem p, const T* __re
 }
 
 template <int D>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_mfma_kernel(Problem p, FwdArgs a,
-                                                                   const float* __restrict__ bias_s, int nqp,
-                                                                   int nkp) {
-  constexpr int KS = D >= 16 ? D / 16 : 1;  // 16-deep steps of the Q.K contraction
-  constexpr int DB = D >= 32 ? D / 32 : 1;  // 32-row blocks of O^T
-  constexpr int KROW = KS * 16 + 8;         // bf16 per staged K row (8 padding)
-  constexpr int VROW = kFwdKeys + 8;        // bf16 per staged V^T row (8 padding)
-  constexpr int CHUNKS = D / 8;             // 16-byte chunks per key row
-  __shared__ __align__(16) uint16_t k_lds[kFwdKeys * KROW];
-  __shared__ __align__(16) uint16_t vt_lds[DB * 32 * VROW];
-  __shared__ __align__(16) float m_lds[kFwdKeys];
+__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(Problem p, FwdArgs a, const float* __restrict__ bias_s,
+                                                               int np) {
+  using S = Shape<D>;
+  constexpr int kFwdRows = fwd_rows<D>();
+  constexpr int KROW = S::ROW;    // K rows, read as b128 operands
+  constexpr int VROW = S::TRROW;  // V rows, read with transposing loads
+  __shared__ __align__(16) uint16_t k_lds[2][kFwdRows][kStep * KROW];
+  __shared__ __align__(16) uint16_t v_lds[2][kFwdRows][kStep * VROW];
+  __shared__ __align__(16) float m_lds[2][kFwdRows][kStep];
 
   const int nqb = (p.N + kFwdQueries - 1) / kFwdQueries;
   int blk = blockIdx.x;
   const int qb = blk % nqb;
   blk /= nqb;
   const int h = blk % p.H;
-  const int r = blk / p.H;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  const int rp = blk / p.H;  // row group: rows kFwdRows * rp + i
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int j0 = qb * kFwdQueries + wave * 32;
-  const int j = j0 + col;  // this lane's query
+  const int j = j0 + col;  // this lane's query (< np)
   const bool wave_active = j0 < p.N;
 
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* k = static_cast<const uint16_t*>(a.k);
-  const uint16_t* v = static_cast<const uint16_t*>(a.v);
   const float sd = sqrtf(static_cast<float>(D));
   const float c1 = kLog2e / sd;
+  const int64_t pstep = pos_step(p);
 
-  // Q as the B operand of S^T = K Q^T: query = col, d = 16 ks + 8 half + i.
-  u32x4 qreg[KS];
+  int rr[kFwdRows];
+  bool rvalid[kFwdRows];
+  const uint16_t* kbase[kFwdRows];
+  const uint16_t* vbase[kFwdRows];
+  const float* mrow[kFwdRows];
+  u32x4 qreg[kFwdRows][S::KS];
+  f32x16 oacc[kFwdRows][S::DB];
+  float m_run[kFwdRows], l_run[kFwdRows];
+  Stage<D> kst[kFwdRows], vst[kFwdRows];
+  float mnext[kFwdRows];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int d0 = ks * 16 + 8 * half;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (j < p.N && d0 < D) val = *reinterpret_cast<const u32x4*>(q + elem_offset(p, r, j, h) + d0);
-    qreg[ks] = val;
+  for (int i = 0; i < kFwdRows; ++i) {
+    rvalid[i] = kFwdRows * rp + i < p.R;
+    rr[i] = rvalid[i] ? kFwdRows * rp + i : kFwdRows * rp;  // an invalid row aliases a valid one
+    const int64_t rh = row_head_offset(p, rr[i], h);
+    kbase[i] = static_cast<const uint16_t*>(a.k) + rh;
+    vbase[i] = static_cast<const uint16_t*>(a.v) + rh;
+    mrow[i] = a.mask ? a.mask + static_cast<int64_t>(rr[i]) * p.N : nullptr;
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks)
+      qreg[i][ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.q), rr[i], j, h, ks, half);
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[i][db][e] = 0.f;
+    m_run[i] = -INFINITY;  // running max of this query's logits, log2 units
+    l_run[i] = 0.f;        // this lane's share of the running sum
+    kst[i].init(p);
+    vst[i].init(p);
+    kst[i].load(kbase[i], 0, p.N);
+    vst[i].load(vbase[i], 0, p.N);
+    mnext[i] = mrow[i] ? mrow[i][min(lane, p.N - 1)] : 0.f;
   }
 
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY;  // running max of the scaled (log2) logits of this query
-  float l_run = 0.f;        // this lane's share of the running sum
+  // The scaled bias of the next block, shared by the rows of the group.
+  const float* bhead = bias_s + static_cast<int64_t>(h) * np * np;  // uniform
+  const uint32_t boff = static_cast<uint32_t>(j * np);              // per lane
+  f32x16 bnext[2];
+  bnext[0] = load_acc_rows(bhead + boff, half);
+  bnext[1] = load_acc_rows(bhead + boff + 32, half);
 
-  const float* brow = bias_s + (static_cast<int64_t>(h) * nqp + j) * nkp;
-  const float* mrow = a.mask ? a.mask + static_cast<int64_t>(r) * p.N : nullptr;
-
-  for (int k0 = 0; k0 < p.N; k0 += kFwdKeys) {
-    // Classify the block by its mask (same answer in every wave of the workgroup).
-    const int key = k0 + lane;
-    const bool valid = key < p.N;
-    const float mv = (mrow && valid) ? mrow[key] : 0.f;
-    const uint64_t live = __ballot(valid && mv != -INFINITY);
-    if (live == 0) continue;
-    const bool any_mask = __ballot(valid && mv != 0.f) != 0;
-
-    __syncthreads();  // the previous block's LDS readers are done
-    for (int c = tid; c < kFwdKeys * CHUNKS; c += kFwdThreads) {
-      const int kr = c / CHUNKS;
-      const int ch = c % CHUNKS;
-      const int kk = k0 + kr;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (kk < p.N) {
-        const int64_t off = elem_offset(p, r, kk, h) + ch * 8;
-        kv = *reinterpret_cast<const u32x4*>(k + off);
-        vv = *reinterpret_cast<const u32x4*>(v + off);
-      }
-      *reinterpret_cast<u32x4*>(&k_lds[kr * KROW + ch * 8]) = kv;
+  int buf = 0;
+  for (int k0 = 0; k0 < p.N; k0 += kStep) {
+    // Classify the block by its mask (the same in every wave of the workgroup).
+    const bool valid = k0 + lane < p.N;
+    bool any_mask[kFwdRows];
+    float mv[kFwdRows];
+    bool any_live = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vt_lds[(ch * 8 + 2 * i) * VROW + kr] = static_cast<uint16_t>(vv[i] & 0xffffu);
-        vt_lds[(ch * 8 + 2 * i + 1) * VROW + kr] = static_cast<uint16_t>(vv[i] >> 16);
-      }
+    for (int i = 0; i < kFwdRows; ++i) {
+      mv[i] = valid ? mnext[i] : 0.f;
+      any_live = any_live || (rvalid[i] && __ballot(valid && mv[i] != -INFINITY) != 0);
+      any_mask[i] = __ballot(mv[i] != 0.f) != 0;
     }
-    if (any_mask && tid < kFwdKeys) m_lds[tid] = valid ? sd * mv : -INFINITY;
-    __syncthreads();
-    if (!wave_active) continue;
-
-    // S^T tiles for keys k0 + [0,32) and k0 + [32,64).
-    f32x16 s[2];
+    const int k1 = k0 + kStep;
+    if (!any_live) {  // every key of the block is masked in every row of the group
+      if (k1 < p.N) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(brow + k0 + mb * 32 + 8 * g + 4 * half);
-        s[mb][4 * g + 0] = b4[0];
-        s[mb][4 * g + 1] = b4[1];
-        s[mb][4 * g + 2] = b4[2];
-        s[mb][4 * g + 3] = b4[3];
-      }
-      if (any_mask) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 m4 = *reinterpret_cast<const f32x4*>(&m_lds[mb * 32 + 8 * g + 4 * half]);
-          s[mb][4 * g + 0] += m4[0];
-          s[mb][4 * g + 1] += m4[1];
-          s[mb][4 * g + 2] += m4[2];
-          s[mb][4 * g + 3] += m4[3];
+        for (int i = 0; i < kFwdRows; ++i) {
+          kst[i].load(kbase[i] + k1 * pstep, k1, p.N);
+          vst[i].load(vbase[i] + k1 * pstep, k1, p.N);
+          if (mrow[i]) mnext[i] = mrow[i][min(k1 + lane, p.N - 1)];
         }
+        bnext[0] = load_acc_rows(bhead + k1 + boff, half);
+        bnext[1] = load_acc_rows(bhead + k1 + boff + 32, half);
       }
+      continue;
+    }
+    const int cb = buf;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 kop = {0u, 0u, 0u, 0u};
-        if (D >= 16 || half == 0) kop = *reinterpret_cast<const u32x4*>(&k_lds[(mb * 32 + col) * KROW + ks * 16 + 8 * half]);
-        s[mb] = mma(kop, qreg[ks], s[mb]);
+    for (int i = 0; i < kFwdRows; ++i) {
+      kst[i].store(k_lds[buf][i], nullptr, KROW, k0, p.N);
+      vst[i].store(v_lds[buf][i], nullptr, VROW, k0, p.N);
+      if (any_mask[i] && tid < kStep) m_lds[buf][i][tid] = valid ? sd * mv[i] : -INFINITY;
+    }
+    lds_barrier();
+    buf ^= 1;
+
+    // S^T tiles (keys k0 + 32 mb + ..., lane = query) of every row; the prefetched
+    // sqrt(d) * bias registers are the first MFMA's accumulator input.
+    f32x16 s[kFwdRows][2];
+#pragma unroll
+    for (int i = 0; i < kFwdRows; ++i) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 a0 = rows_operand<D>(k_lds[cb][i], mb * 32, 0, col, half);
+        if (any_mask[i])
+          s[i][mb] = mma(a0, qreg[i][0], bnext[mb] + load_acc_rows(&m_lds[cb][i][mb * 32], half));
+        else
+          s[i][mb] = mma(a0, qreg[i][0], bnext[mb]);
+#pragma unroll
+        for (int ks = 1; ks < S::KS; ++ks)
+          s[i][mb] = mma(rows_operand<D>(k_lds[cb][i], mb * 32, ks, col, half), qreg[i][ks], s[i][mb]);
       }
     }
 
-    // Online softmax over this block's keys (exp2 domain).
-    float mx = s[0][0];
+    // Prefetch the next block; overlaps the softmax and P V below.
+    if (k1 < p.N) {
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx * c1);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-
-    u32x4 pb[2][2];  // P^T packed to bf16: [key tile][16-key half]
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float pv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pv[i] = fast_exp2(__builtin_fmaf(s[mb][8 * t + i], c1, -m_new));
-          l_run += pv[i];
-        }
-        pb[mb][t] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
-                          pack_bf16(pv[6], pv[7])};
+      for (int i = 0; i < kFwdRows; ++i) {
+        kst[i].load(kbase[i] + k1 * pstep, k1, p.N);
+        vst[i].load(vbase[i] + k1 * pstep, k1, p.N);
+        if (mrow[i]) mnext[i] = mrow[i][min(k1 + lane, p.N - 1)];
       }
+      bnext[0] = load_acc_rows(bhead + k1 + boff, half);
+      bnext[1] = load_acc_rows(bhead + k1 + boff + 32, half);
     }
 
-    // O^T += V^T P^T over the 64 keys (four 16-deep steps).
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint16_t* vrow = &vt_lds[(db * 32 + col) * VROW];
+    for (int i = 0; i < kFwdRows; ++i) {
+      // Online softmax over this block's keys (exp2 domain).  A row whose keys
+      // are all masked so far keeps m = -inf; its exponent base is then 0, so
+      // every P of the block is exp2(-inf) = 0.
+      const float mx = pair_max(tile_max(s[i][0], s[i][1]));
+      const float m_new = fmaxf(m_run[i], mx * c1);
+      if (__ballot(m_new != m_run[i]) != 0) {  // some query's max grew: rescale
+        const float alpha = fast_exp2(m_run[i] - m_new);
+        l_run[i] *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) oacc[i][db] *= alpha;
+      }
+      m_run[i] = m_new;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+
+      u32x4 pb[2][2];  // P^T packed to bf16: [key tile][16-key half]
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int kb0 = mb * 32 + 16 * t + 4 * half;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb0);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kb0 + 8);
-          oacc[db] = mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[mb][t], oacc[db]);
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[i][mb][8 * t + e], c1, -m_use));
+          pb[mb][t] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                            pack_bf16(pv[6], pv[7])};
         }
       }
+      // Row sum of the bf16 probabilities that enter P V (four independent chains).
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ls[e] = add_bf16_pair(pb[mb][t][e], ls[e]);
+      l_run[i] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+      // O^T += V^T P^T over the 64 keys (four 16-deep steps per 32-row block of d).
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            oacc[i][db] = mma(tr_operand<D>(v_lds[cb][i], VROW, db, mb * 32, t, lane), pb[mb][t], oacc[i][db]);
     }
   }
 
   if (!wave_active) return;
-  const float l_tot = pair_sum(l_run);
-  if (j >= p.N) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* o = static_cast<uint16_t*>(a.o) + elem_offset(p, r, j, h);
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = db * 32 + 8 * g + 4 * half;
-      if (d < D) {
-        const u32x2 w = {pack_bf16(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                         pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(o + d) = w;
-      }
-    }
+  for (int i = 0; i < kFwdRows; ++i) {
+    const float l_tot = pair_sum(l_run[i]);
+    if (j >= p.N || !rvalid[i]) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    store_dT<D>(static_cast<uint16_t*>(a.o) + elem_offset(p, rr[i], j, h), oacc[i], inv, half);
+    if (a.lse && half == 0)
+      a.lse[(static_cast<int64_t>(rr[i]) * p.H + h) * p.N + j] =
+          l_tot > 0.f ? (m_run[i] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
-  if (a.lse && half == 0)
-    a.lse[(static_cast<int64_t>(r) * p.H + h) * p.N + j] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D>
 hipError_t fwd_mfma_dispatch(const Problem& p, const FwdArgs& a, float* bias_s, int np, hipStream_t s) {
   hipError_t e = launch_bias_prep(p, a.bias, bias_s, np, 0, s);
   if (e != hipSuccess) return e;
-  const int64_t blocks = static_cast<int64_t>((p.N + kFwdQueries - 1) / kFwdQueries) * p.H * p.R;
+  constexpr int rows = fwd_rows<D>();
+  const int64_t blocks =
+      static_cast<int64_t>((p.N + kFwdQueries - 1) / kFwdQueries) * p.H * ((p.R + rows - 1) / rows);
   KernelTimer timer("fwd_mfma", s);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kFwdThreads), 0, s, p, a,
-                     bias_s, np, np);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p, a,
+                     bias_s, np);
   return hipGetLastError();
 }
 

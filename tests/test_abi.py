@@ -53,7 +53,10 @@ def test_version_and_status_strings():
 
 def test_workspace_queries():
     lib = _lib.load()
-    assert lib.evoattn_fwd_workspace_bytes(384, 384, 4, 32, 1) == 0
+    fws = lib.evoattn_fwd_workspace_bytes(384, 384, 4, 32, 1)
+    assert fws % 256 == 0
+    assert fws <= 4 * 512 * 512 * 4          # one padded fp32 copy of the bias at most
+    assert lib.evoattn_fwd_workspace_bytes(64, 64, 4, 32, 0) == 0   # fp32 path needs none
     ws = lib.evoattn_bwd_workspace_bytes(384, 384, 4, 32, 1)
     assert ws >= 384 * 4 * 384 * 4            # at least the per-row statistics
     assert ws % 256 == 0
@@ -71,7 +74,7 @@ A = 1 << 20
 def fwd(**kw):
     lib = _lib.load()
     args = dict(rows=4, n=8, heads=2, head_dim=32, dtype=1, transpose=0, q=A, k=A, v=A, bias=None, mask=None,
-                o=A, lse=A, ws=None, ws_bytes=0)
+                o=A, lse=A, ws=A, ws_bytes=1 << 30)
     args.update(kw)
     return lib.evoattn_fwd(args["rows"], args["n"], args["heads"], args["head_dim"], args["dtype"],
                            args["transpose"], args["q"], args["k"], args["v"], args["bias"], args["mask"],
@@ -108,6 +111,9 @@ def detail():
     (dict(k=A + 2), INVALID, "aligned"),
     (dict(bias=A + 8), INVALID, "aligned"),
     (dict(mask=A + 2), INVALID, "aligned"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(ws_bytes=16), WORKSPACE, "workspace"),
+    (dict(ws=A + 64), INVALID, "256-byte"),
 ])
 def test_fwd_validation(kw, code, needle):
     assert fwd(**kw) == code

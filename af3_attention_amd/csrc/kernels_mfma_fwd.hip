@@ -7,242 +7,293 @@
 // R*H*N*N logit tensor never reaches HBM; the pair bias is added to every row.
 //
 // Mapping to CDNA4:
-//  * one workgroup = 4 waves = 128 queries of one (row r, head h); each wave owns
-//    32 queries and walks the keys in blocks of 64;
-//  * the logits are produced transposed, S^T = K Q^T (keys x queries), so each
-//    lane holds 32 keys of one query: the softmax max and sum over keys are
-//    in-lane reductions plus one exchange with lane l ^ 32;
-//  * the MFMA accumulator starts from sqrt(d) * (bias + mask) in fp32 (a
-//    pre-pass writes the scaled bias once per call), so bias and mask cost no
-//    vector ALU work; one FMA per logit applies log2(e)/sqrt(d) and subtracts
-//    the running max before the exp2;
-//  * P^T stays in registers and is, after packing to bf16, directly the B
-//    operand of O^T = V^T P^T; V is staged transposed in LDS;
-//  * key blocks whose keys are all masked are skipped; blocks with no masked
-//    key skip the mask add.
+//  * one workgroup = 4 waves = 128 queries of two rows (r, r+1) of one head; each
+//    wave owns 32 queries of both rows, so every bias tile it loads serves two rows;
+//  * keys are walked in blocks of 64 through a four-stage LDS ring filled by
+//    direct global -> LDS copies (no register staging) two blocks ahead, with one
+//    workgroup barrier per block;
+//  * the logits are produced transposed, S^T = K Q^T (keys x queries), so each lane
+//    holds 32 keys of one query: the softmax max and sum are in-lane reductions
+//    plus one exchange with lane l ^ 32;
+//  * the softmax keeps a lazily refreshed reference point (the exponentials of a
+//    block may exceed 1 until a lane's block sum crosses a bound), so a block
+//    normally costs one FMA, one exp2, half a pack and half a dot2 per logit and
+//    no max reduction or rescale;
+//  * the MFMA accumulator starts from sqrt(d) * bias, read as four coalesced 1 KB
+//    loads from a pre-pass's tiled copy, so the bias costs no vector ALU work;
+//    one FMA per logit applies log2(e)/sqrt(d) and subtracts the running max;
+//  * P^T stays in registers and, packed to bf16, is directly the B operand of
+//    O^T = V^T P^T; V^T comes from transposing LDS reads (ds_read_b64_tr_b16);
+//  * key blocks whose keys are all masked in both rows are skipped; blocks with no
+//    masked key skip the mask add.
+//  * workgroups are mapped so that each XCD works on one contiguous range of
+//    (head, row pair) and its L2 holds one head's bias and the rows' K, V.
 
 #include <algorithm>
+#include <type_traits>
 
-#include "mfma_common.h"
+#include "pipe_common.h"
 
 namespace evo {
 namespace {
 
 using namespace mfma;
+using namespace pipe;
 
 constexpr int kFwdQueries = 128;  // queries per workgroup (32 per wave)
-// Attention rows per wave; the rows of a wave share each load of the bias tile.
-template <int D>
-constexpr int fwd_rows() { return D <= 32 ? 2 : 1; }
+constexpr int kFwdRows = 2;       // attention rows per workgroup
+constexpr int kStages = 4;  // LDS ring of K/V stages (copies run two blocks ahead)
 
-// out[h][j][k] = sqrt(d) * bias[h][j][k] for j, k < N; -inf for k >= N (padding keys
-// never win the softmax); 0 for padding queries.  Row stride nk, nq rows per head.
-// transpose_out writes out[h][k][j] instead (the layout the backward's S tiles need).
-template <typename T>
-__global__ __launch_bounds__(256) void bias_prep_kernel(Problem p, const T* __restrict__ bias, float* __restrict__ out,
-                                                        int nq, int nk, int transpose_out) {
-  const int64_t total = static_cast<int64_t>(p.H) * nq * nk;
-  const float sd = sqrtf(static_cast<float>(p.D));
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int inner = static_cast<int>(idx % nk);
-    const int outer = static_cast<int>((idx / nk) % nq);
-    const int h = static_cast<int>(idx / (static_cast<int64_t>(nk) * nq));
-    const int j = transpose_out ? inner : outer;
-    const int k = transpose_out ? outer : inner;
-    float val;
-    if (k >= p.N) {
-      val = -INFINITY;
-    } else if (j >= p.N || bias == nullptr) {
-      val = 0.f;
-    } else {
-      val = sd * Elem<T>::load(bias, (static_cast<int64_t>(h) * p.N + j) * p.N + k);
-    }
-    out[idx] = val;
+// Largest of the 32 values of two accumulator tiles (v_max3 chains; inputs are
+// finite or -inf, never NaN).
+__device__ __forceinline__ float max_of_tiles(const f32x16& a, const f32x16& b) {
+  float m[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    m[u] = max3f(a[4 * u], a[4 * u + 1], a[4 * u + 2]);
+    m[u] = max3f(m[u], a[4 * u + 3], b[4 * u]);
+    m[u] = max3f(m[u], b[4 * u + 1], b[4 * u + 2]);
+    m[u] = max3f(m[u], b[4 * u + 3], b[4 * u + 3]);
   }
+  return max3f(m[0], m[1], max3f(m[2], m[3], m[3]));
 }
 
+__device__ __forceinline__ float pair_max_raw(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
+
+// A block's probabilities may exceed 1 by up to this factor before the running
+// maximum is refreshed (the normalised result does not depend on the reference
+// point; fp32 and bf16 keep the full range).
+constexpr float kLazyMaxSum = 1048576.f;  // 2^20, bound on one lane's 32-term block sum
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(Problem p, FwdArgs a, const float* __restrict__ bias_s,
-                                                               int np) {
-  using S = Shape<D>;
-  constexpr int kFwdRows = fwd_rows<D>();
-  constexpr int KROW = S::ROW;    // K rows, read as b128 operands
-  constexpr int VROW = S::TRROW;  // V rows, read with transposing loads
-  __shared__ __align__(16) uint16_t k_lds[2][kFwdRows][kStep * KROW];
-  __shared__ __align__(16) uint16_t v_lds[2][kFwdRows][kStep * VROW];
-  __shared__ __align__(16) float m_lds[2][kFwdRows][kStep];
+__global__ __launch_bounds__(256, 2) void fwd_pipe_kernel(Problem p, FwdArgs a, const float* __restrict__ bias_t,
+                                                          int nt) {
+  constexpr int TB = Tile<D>::BYTES;
+  constexpr int NT = 2 * kFwdRows;  // staged tiles per stage: K, V of each row
+  constexpr int STAGE = NT * TB;
+  using St = Stager<D, NT>;
+  constexpr int NDMA = St::NIT;
+  constexpr int KS = Shape<D>::KS, DB = Shape<D>::DB;
+  __shared__ __align__(16) char lds[kStages * STAGE];
+  __shared__ __align__(16) float mlds[kStages][kFwdRows][kBlk];
 
   const int nqb = (p.N + kFwdQueries - 1) / kFwdQueries;
-  int blk = blockIdx.x;
+  const int nrg = (p.R + kFwdRows - 1) / kFwdRows;
+  int blk = xcd_logical_block(blockIdx.x, nqb * nrg * p.H);
   const int qb = blk % nqb;
   blk /= nqb;
-  const int h = blk % p.H;
-  const int rp = blk / p.H;  // row group: rows kFwdRows * rp + i
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int rg = blk % nrg;
+  const int h = blk / nrg;
+  const int wave = wave_id(), lane = threadIdx.x & 63, half = lane >> 5;
   const int j0 = qb * kFwdQueries + wave * 32;
-  const int j = j0 + col;  // this lane's query (< np)
+  const int j = j0 + (lane & 31);  // this lane's query
   const bool wave_active = j0 < p.N;
+  const int nkb = (p.N + kBlk - 1) / kBlk;
 
   const float sd = sqrtf(static_cast<float>(D));
   const float c1 = kLog2e / sd;
-  const int64_t pstep = pos_step(p);
 
   int rr[kFwdRows];
   bool rvalid[kFwdRows];
-  const uint16_t* kbase[kFwdRows];
-  const uint16_t* vbase[kFwdRows];
+  const char* tbase[NT];  // K r0, V r0, K r1, V r1
   const float* mrow[kFwdRows];
-  u32x4 qreg[kFwdRows][S::KS];
-  f32x16 oacc[kFwdRows][S::DB];
+  u32x4 qreg[kFwdRows][KS];
+  f32x16 oacc[kFwdRows][DB];
   float m_run[kFwdRows], l_run[kFwdRows];
-  Stage<D> kst[kFwdRows], vst[kFwdRows];
-  float mnext[kFwdRows];
 #pragma unroll
   for (int i = 0; i < kFwdRows; ++i) {
-    rvalid[i] = kFwdRows * rp + i < p.R;
-    rr[i] = rvalid[i] ? kFwdRows * rp + i : kFwdRows * rp;  // an invalid row aliases a valid one
+    rvalid[i] = kFwdRows * rg + i < p.R;
+    rr[i] = rvalid[i] ? kFwdRows * rg + i : kFwdRows * rg;  // an invalid row aliases a valid one
     const int64_t rh = row_head_offset(p, rr[i], h);
-    kbase[i] = static_cast<const uint16_t*>(a.k) + rh;
-    vbase[i] = static_cast<const uint16_t*>(a.v) + rh;
-    mrow[i] = a.mask ? a.mask + static_cast<int64_t>(rr[i]) * p.N : nullptr;
+    tbase[2 * i] = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + rh));
+    tbase[2 * i + 1] = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + rh));
+    mrow[i] = a.mask ? uniform_ptr(a.mask + static_cast<int64_t>(rr[i]) * p.N) : nullptr;
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
       qreg[i][ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.q), rr[i], j, h, ks, half);
 #pragma unroll
-    for (int db = 0; db < S::DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[i][db][e] = 0.f;
-    m_run[i] = -INFINITY;  // running max of this query's logits, log2 units
+    m_run[i] = -INFINITY;  // reference point of this query's exponentials, log2 units
     l_run[i] = 0.f;        // this lane's share of the running sum
-    kst[i].init(p);
-    vst[i].init(p);
-    kst[i].load(kbase[i], 0, p.N);
-    vst[i].load(vbase[i], 0, p.N);
-    mnext[i] = mrow[i] ? mrow[i][min(lane, p.N - 1)] : 0.f;
+  }
+  const bool masked = a.mask != nullptr;
+  const uint32_t lds0 = lds_addr(lds), mlds0 = lds_addr(mlds);
+  St stager;
+  stager.init(wave, lane, static_cast<uint32_t>(p.pos_stride * p.H * D * 2));
+  TileReads<D> rd;
+  rd.init(lane);
+
+  // Bias tiles of this wave's 32 queries: tile (qt, kt) of head h.
+  const int qt = qb * (kFwdQueries / 32) + wave;
+  const float* btile = bias_t + bias_tile_offset(h, min(qt, nt - 1), 0, nt);
+  f32x16 bias_reg[2][2];  // two register sets: block kb uses set kb % 2, loaded two blocks ahead
+
+  // Copies of stage kb % kStages: K and V of both rows, and (waves 0 and 1) the
+  // mask of row `wave` for the block's 64 keys (keys >= N read key N - 1).
+  auto issue_stage = [&](int kb, auto stage_c) {
+    constexpr int sn = decltype(stage_c)::value;
+    stager.issue(lds0 + sn * STAGE, tbase, kb * kBlk, p.N, wave);
+    if (masked && wave < kFwdRows) {
+      const uint32_t dst = mlds0 + (sn * kFwdRows + wave) * kBlk * 4;
+      const float* m = wave == 0 ? mrow[0] : mrow[1];
+      if (kb * kBlk + kBlk <= p.N)
+        copy4_to_lds(uniform_ptr(m + kb * kBlk), static_cast<uint32_t>(lane) * 4, dst);
+      else
+        copy4_to_lds(m + min(kb * kBlk + lane, p.N - 1), dst);
+    }
+  };
+
+  auto load_bias = [&](f32x16 (&dst)[2], int kb) {
+    dst[0] = load_bias_tile(btile + (2 * kb) * 1024, lane);
+    dst[1] = load_bias_tile(btile + (2 * kb + 1) * 1024, lane);
+  };
+
+  // Prologue: bias and stage of blocks 0 and 1, in the order of the loop body.
+  load_bias(bias_reg[0], 0);
+  issue_stage(0, std::integral_constant<int, 0>());
+  if (nkb > 1) {
+    load_bias(bias_reg[1], 1);
+    issue_stage(1, std::integral_constant<int, 1>());
   }
 
-  // The scaled bias of the next block, shared by the rows of the group.
-  const float* bhead = bias_s + static_cast<int64_t>(h) * np * np;  // uniform
-  const uint32_t boff = static_cast<uint32_t>(j * np);              // per lane
-  f32x16 bnext[2];
-  bnext[0] = load_acc_rows(bhead + boff, half);
-  bnext[1] = load_acc_rows(bhead + boff + 32, half);
+  // One block of 64 keys; its stage index is a compile-time constant (the loop
+  // below is unrolled by kStages) so every LDS address is a fixed offset.
+  auto step = [&](auto stage_c, int kb) {
+    constexpr int st = decltype(stage_c)::value;
+    // Stage kb was issued two blocks ago; after it this wave issued the bias
+    // loads (8) and the stage of block kb + 1, if there is one.
+    if (kb + 1 < nkb)
+      wait_vmcnt<8 + NDMA>();
+    else
+      wait_vmcnt<0>();
+    barrier();
+    uint32_t kt_lds[kFwdRows], vt_lds[kFwdRows];
+#pragma unroll
+    for (int i = 0; i < kFwdRows; ++i) {
+      kt_lds[i] = lds0 + st * STAGE + (2 * i) * TB;
+      vt_lds[i] = lds0 + st * STAGE + (2 * i + 1) * TB;
+    }
 
-  int buf = 0;
-  for (int k0 = 0; k0 < p.N; k0 += kStep) {
-    // Classify the block by its mask (the same in every wave of the workgroup).
-    const bool valid = k0 + lane < p.N;
+    // Classify the block by its mask (identical in every wave); keys >= N are dead.
     bool any_mask[kFwdRows];
-    float mv[kFwdRows];
-    bool any_live = false;
-#pragma unroll
-    for (int i = 0; i < kFwdRows; ++i) {
-      mv[i] = valid ? mnext[i] : 0.f;
-      any_live = any_live || (rvalid[i] && __ballot(valid && mv[i] != -INFINITY) != 0);
-      any_mask[i] = __ballot(mv[i] != 0.f) != 0;
-    }
-    const int k1 = k0 + kStep;
-    if (!any_live) {  // every key of the block is masked in every row of the group
-      if (k1 < p.N) {
-#pragma unroll
-        for (int i = 0; i < kFwdRows; ++i) {
-          kst[i].load(kbase[i] + k1 * pstep, k1, p.N);
-          vst[i].load(vbase[i] + k1 * pstep, k1, p.N);
-          if (mrow[i]) mnext[i] = mrow[i][min(k1 + lane, p.N - 1)];
-        }
-        bnext[0] = load_acc_rows(bhead + k1 + boff, half);
-        bnext[1] = load_acc_rows(bhead + k1 + boff + 32, half);
-      }
-      continue;
-    }
-    const int cb = buf;
-#pragma unroll
-    for (int i = 0; i < kFwdRows; ++i) {
-      kst[i].store(k_lds[buf][i], nullptr, KROW, k0, p.N);
-      vst[i].store(v_lds[buf][i], nullptr, VROW, k0, p.N);
-      if (any_mask[i] && tid < kStep) m_lds[buf][i][tid] = valid ? sd * mv[i] : -INFINITY;
-    }
-    lds_barrier();
-    buf ^= 1;
-
-    // S^T tiles (keys k0 + 32 mb + ..., lane = query) of every row; the prefetched
-    // sqrt(d) * bias registers are the first MFMA's accumulator input.
-    f32x16 s[kFwdRows][2];
-#pragma unroll
-    for (int i = 0; i < kFwdRows; ++i) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 a0 = rows_operand<D>(k_lds[cb][i], mb * 32, 0, col, half);
-        if (any_mask[i])
-          s[i][mb] = mma(a0, qreg[i][0], bnext[mb] + load_acc_rows(&m_lds[cb][i][mb * 32], half));
-        else
-          s[i][mb] = mma(a0, qreg[i][0], bnext[mb]);
-#pragma unroll
-        for (int ks = 1; ks < S::KS; ++ks)
-          s[i][mb] = mma(rows_operand<D>(k_lds[cb][i], mb * 32, ks, col, half), qreg[i][ks], s[i][mb]);
-      }
-    }
-
-    // Prefetch the next block; overlaps the softmax and P V below.
-    if (k1 < p.N) {
+    bool any_live = !masked;
+    const bool kvalid = kb * kBlk + lane < p.N;
+    if (masked) {
 #pragma unroll
       for (int i = 0; i < kFwdRows; ++i) {
-        kst[i].load(kbase[i] + k1 * pstep, k1, p.N);
-        vst[i].load(vbase[i] + k1 * pstep, k1, p.N);
-        if (mrow[i]) mnext[i] = mrow[i][min(k1 + lane, p.N - 1)];
+        const float mv = mlds[st][i][lane];
+        any_mask[i] = __ballot(kvalid && mv != 0.f) != 0;
+        any_live = any_live || (rvalid[i] && __ballot(kvalid && mv != -INFINITY) != 0);
       }
-      bnext[0] = load_acc_rows(bhead + k1 + boff, half);
-      bnext[1] = load_acc_rows(bhead + k1 + boff + 32, half);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kFwdRows; ++i) any_mask[i] = false;
     }
+    const bool compute = any_live && wave_active;
+    f32x16 (&bcur)[2] = bias_reg[st % 2];
 
+    // S^T tiles (keys 32 mb + .., lane = query) of both rows; the bias registers
+    // are the first MFMA's accumulator input.
+    f32x16 s[kFwdRows][2];
+    if (compute) {
 #pragma unroll
-    for (int i = 0; i < kFwdRows; ++i) {
-      // Online softmax over this block's keys (exp2 domain).  A row whose keys
-      // are all masked so far keeps m = -inf; its exponent base is then 0, so
-      // every P of the block is exp2(-inf) = 0.
-      const float mx = pair_max(tile_max(s[i][0], s[i][1]));
-      const float m_new = fmaxf(m_run[i], mx * c1);
-      if (__ballot(m_new != m_run[i]) != 0) {  // some query's max grew: rescale
-        const float alpha = fast_exp2(m_run[i] - m_new);
-        l_run[i] *= alpha;
+      for (int i = 0; i < kFwdRows; ++i) {
 #pragma unroll
-        for (int db = 0; db < S::DB; ++db) oacc[i][db] *= alpha;
-      }
-      m_run[i] = m_new;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-
-      u32x4 pb[2][2];  // P^T packed to bf16: [key tile][16-key half]
+        for (int mb = 0; mb < 2; ++mb) {
+          const u32x4 a0 = rd.rows_operand(kt_lds[i], mb * 32, 0, lane);
+          if (any_mask[i])
+            s[i][mb] = mma(a0, qreg[i][0], bcur[mb] + sd * lds_acc_rows(mlds0 + ((st * kFwdRows + i) * kBlk + mb * 32) * 4, half));
+          else
+            s[i][mb] = mma(a0, qreg[i][0], bcur[mb]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[i][mb][8 * t + e], c1, -m_use));
-          pb[mb][t] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
-                            pack_bf16(pv[6], pv[7])};
+          for (int ks = 1; ks < KS; ++ks)
+            s[i][mb] = mma(rd.rows_operand(kt_lds[i], mb * 32, ks, lane), qreg[i][ks], s[i][mb]);
         }
       }
-      // Row sum of the bf16 probabilities that enter P V (four independent chains).
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ls[e] = add_bf16_pair(pb[mb][t][e], ls[e]);
-      l_run[i] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-
-      // O^T += V^T P^T over the 64 keys (four 16-deep steps per 32-row block of d).
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            oacc[i][db] = mma(tr_operand<D>(v_lds[cb][i], VROW, db, mb * 32, t, lane), pb[mb][t], oacc[i][db]);
     }
+
+    // A skipped block still retires its bias loads here, so that every path
+    // reaches the next loads with no outstanding write to the bias registers.
+    if (!compute) asm volatile("" ::"v"(bcur[0]), "v"(bcur[1]));
+
+    // Prefetch block kb + 2: its bias into the registers block kb just used, then
+    // its stage (that buffer was last read in iteration kb - 2).  Bias loads go
+    // first, so that the compiler's wait for them at block kb + 2 leaves the
+    // stage of block kb + 3 in flight.
+    if (kb + 2 < nkb) {
+      load_bias(bcur, kb + 2);
+      issue_stage(kb + 2, std::integral_constant<int, (st + 2) % kStages>());
+    }
+
+    if (compute) {
+#pragma unroll
+      for (int i = 0; i < kFwdRows; ++i) {
+        // Online softmax (exp2 domain) with a lazily refreshed reference point m:
+        // P = exp2(S c1 - m).  While m is finite and no lane's 32-term block sum
+        // exceeds kLazyMaxSum, the block is accumulated against the current m; else
+        // m moves to the running maximum and the accumulators are rescaled.  A row
+        // whose keys are all masked so far keeps m = -inf and gets P = 0.
+        u32x4 pb[2][2];  // P^T packed to bf16: [key tile][16-key half]
+        float lsum;
+        auto exponentiate = [&](float m_use) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              float pv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[i][mb][8 * t + e], c1, -m_use));
+              pb[mb][t] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                                pack_bf16(pv[6], pv[7])};
+            }
+          }
+          // Sum of the bf16 probabilities that enter P V (four independent chains).
+          float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ls[e] = add_bf16_pair(pb[mb][t][e], ls[e]);
+          lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        };
+        const bool fresh = __ballot(m_run[i] == -INFINITY) != 0;
+        if (!fresh) exponentiate(m_run[i]);
+        if (fresh || __ballot(!(lsum <= kLazyMaxSum)) != 0) {
+          const float mx = pair_max_raw(max_of_tiles(s[i][0], s[i][1])) * c1;
+          const float m_new = fmaxf(m_run[i], mx);
+          const float alpha = m_run[i] == -INFINITY ? 0.f : fast_exp2(m_run[i] - m_new);
+          l_run[i] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[i][db] *= alpha;
+          m_run[i] = m_new;
+          exponentiate(m_new == -INFINITY ? 0.f : m_new);
+        }
+        l_run[i] += lsum;
+
+        // O^T += V^T P^T over the 64 keys (four 16-deep steps per 32-row block of d).
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              oacc[i][db] = mma(rd.tr_operand(vt_lds[i], db, mb * 32, t), pb[mb][t], oacc[i][db]);
+      }
+    }
+  };
+
+
+  for (int kb = 0; kb < nkb; kb += kStages) {
+    step(std::integral_constant<int, 0>(), kb);
+    if (kb + 1 < nkb) step(std::integral_constant<int, 1>(), kb + 1);
+    if (kb + 2 < nkb) step(std::integral_constant<int, 2>(), kb + 2);
+    if (kb + 3 < nkb) step(std::integral_constant<int, 3>(), kb + 3);
   }
 
   if (!wave_active) return;
@@ -259,45 +310,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(Problem p, FwdArg
 }
 
 template <int D>
-hipError_t fwd_mfma_dispatch(const Problem& p, const FwdArgs& a, float* bias_s, int np, hipStream_t s) {
-  hipError_t e = launch_bias_prep(p, a.bias, bias_s, np, 0, s);
+hipError_t fwd_pipe_dispatch(const Problem& p, const FwdArgs& a, float* bias_t, hipStream_t s) {
+  hipError_t e = launch_bias_tiles(p, a.bias, bias_t, 0, s);
   if (e != hipSuccess) return e;
-  constexpr int rows = fwd_rows<D>();
-  const int64_t blocks =
-      static_cast<int64_t>((p.N + kFwdQueries - 1) / kFwdQueries) * p.H * ((p.R + rows - 1) / rows);
+  const int64_t blocks = static_cast<int64_t>((p.N + kFwdQueries - 1) / kFwdQueries) * p.H *
+                         ((p.R + kFwdRows - 1) / kFwdRows);
   KernelTimer timer("fwd_mfma", s);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p, a,
-                     bias_s, np);
+  hipLaunchKernelGGL((fwd_pipe_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, a, bias_t,
+                     bias_tiles(p.N));
   return hipGetLastError();
 }
 
 }  // namespace
 
-int bias_pad(int n) { return (n + 127) / 128 * 128; }
-
-hipError_t launch_bias_prep(const Problem& p, const void* bias, float* out, int np, int transpose_out,
-                            hipStream_t s) {
-  const int64_t total = static_cast<int64_t>(p.H) * np * np;
-  const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 8192));
-  KernelTimer timer(transpose_out ? "bias_prep_t" : "bias_prep", s);
-  hipLaunchKernelGGL((bias_prep_kernel<uint16_t>), dim3(blocks), dim3(256), 0, s, p,
-                     static_cast<const uint16_t*>(bias), out, np, np, transpose_out);
-  return hipGetLastError();
-}
-
-size_t fwd_mfma_workspace_bytes(const Problem& p) {
-  const int64_t np = bias_pad(p.N);
-  return static_cast<size_t>(p.H) * np * np * sizeof(float);
-}
+size_t fwd_mfma_workspace_bytes(const Problem& p) { return tiled_bias_bytes(p); }
 
 hipError_t launch_fwd_mfma(const Problem& p, const FwdArgs& a, void* ws, hipStream_t s) {
-  const int np = bias_pad(p.N);
-  float* bias_s = static_cast<float*>(ws);
+  float* bias_t = static_cast<float*>(ws);
   switch (p.D) {
-    case 8: return fwd_mfma_dispatch<8>(p, a, bias_s, np, s);
-    case 16: return fwd_mfma_dispatch<16>(p, a, bias_s, np, s);
-    case 32: return fwd_mfma_dispatch<32>(p, a, bias_s, np, s);
-    case 64: return fwd_mfma_dispatch<64>(p, a, bias_s, np, s);
+    case 8: return fwd_pipe_dispatch<8>(p, a, bias_t, s);
+    case 16: return fwd_pipe_dispatch<16>(p, a, bias_t, s);
+    case 32: return fwd_pipe_dispatch<32>(p, a, bias_t, s);
+    case 64: return fwd_pipe_dispatch<64>(p, a, bias_t, s);
     default: return hipErrorInvalidValue;
   }
 }

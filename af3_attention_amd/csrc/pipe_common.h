@@ -1,0 +1,279 @@
+// Building blocks of the pipelined bf16 MFMA kernels (gfx950): direct
+// global -> LDS copies, the swizzled LDS layout of staged [position][d] tiles,
+// the workgroup -> XCD mapping and the tiled, pre-scaled fp32 bias.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mfma_common.h"
+
+namespace evo {
+namespace pipe {
+
+using namespace mfma;
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Loads through LDS byte addresses (32-bit LDS pointers let the compiler fold
+// constant offsets into the instruction).
+__device__ __forceinline__ u32x4 lds_load16(uint32_t addr) { return *reinterpret_cast<lds_u32x4*>(addr); }
+__device__ __forceinline__ u32x2 lds_load_tr(uint32_t addr) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(addr)));
+}
+// The 16 accumulator registers of a 32-row tile read from an fp32 row vector in
+// LDS: rows 8g + 4 half + (0..3).
+__device__ __forceinline__ f32x16 lds_acc_rows(uint32_t addr, int half) {
+  f32x16 c;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 x = *reinterpret_cast<lds_f32x4*>(addr + 4 * (8 * g + 4 * half));
+    c[4 * g + 0] = x[0];
+    c[4 * g + 1] = x[1];
+    c[4 * g + 2] = x[2];
+    c[4 * g + 3] = x[3];
+  }
+  return c;
+}
+
+// Direct global -> LDS copies (global_load_lds_dword / _dwordx4): lane l's 4 or 16
+// bytes land at lds_wave_base + 4 l or + 16 l (checked on gfx950 hardware).
+// lds_wave_base is an LDS byte address, uniform across the wave.  The copies
+// count in vmcnt like loads.  They are issued from inline assembly so that the
+// compiler does not serialise every later LDS read behind them: the kernels
+// order them explicitly with wait_vmcnt + barrier.  M0 is saved and restored.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_wave_base)
+      : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_wave_base)
+      : "memory");
+}
+
+// The same copies with a uniform 64-bit base (SGPRs) plus a per-lane 32-bit byte
+// offset, which needs no per-lane address arithmetic.
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_wave_base)
+      : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_wave_base)
+      : "memory");
+}
+
+// A pointer that is the same in every lane, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)(p)));
+}
+
+// Waits until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Workgroups are dispatched to the 8 XCDs round robin (block b runs on XCD b % 8),
+// and each XCD has its own L2.  This maps the hardware block index to a logical
+// index such that every XCD receives one contiguous range of logical blocks, so
+// blocks that share data (same head, neighbouring rows) share an L2.
+__device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int q = nblocks >> 3, rem = nblocks & 7;
+  return xcd < rem ? xcd * (q + 1) + slot : rem * (q + 1) + (xcd - rem) * q + slot;
+}
+
+// ---------------------------------------------------------------- staged tiles
+// A staged tile holds kBlk positions x D channels of bf16, row-major by
+// position (2*D bytes per position), in 16-byte chunks.  Chunk p of position x
+// is stored in slot p ^ swz(x) of that position's row so that the MFMA operand
+// reads (16 consecutive positions, same chunk) and the transposing reads hit
+// distinct LDS banks.
+constexpr int kBlk = 64;  // positions per pipeline stage
+
+template <int D>
+struct Tile {
+  static constexpr int CHUNKS = D / 8;            // 16-byte chunks per position
+  static constexpr int BYTES = kBlk * D * 2;      // bytes per staged tile
+  static constexpr int ROWS_PER_256B = 128 / D;   // positions per 256 bytes
+  __device__ __forceinline__ static int swz(int x) {
+    return CHUNKS > 1 ? (x / ROWS_PER_256B) & (CHUNKS - 1) : 0;
+  }
+  // Byte offset of chunk p of position x.
+  __device__ __forceinline__ static int chunk_off(int x, int p) { return x * (2 * D) + ((p ^ swz(x)) << 4); }
+  // Byte offset of channel c (multiple of 4) of position x: 8 bytes hold c..c+3.
+  __device__ __forceinline__ static int quad_off(int x, int c) {
+    return x * (2 * D) + (((c >> 3) ^ swz(x)) << 4) + ((c & 7) << 1);
+  }
+};
+
+// Lane-dependent byte offsets of the MFMA operand reads of a staged tile,
+// computed once per kernel.  Adding a multiple of 16 positions to a read keeps
+// its swizzle, so every read of the main loop is one of these offsets plus a
+// compile-time constant.
+template <int D>
+struct TileReads {
+  static constexpr int KS = Shape<D>::KS, DB = Shape<D>::DB;
+  int rows[KS];    // A operand (rows m = positions 0..31, k = channels 16 ks + 8 half ..)
+  int tr[DB][2];   // transposing reads of positions 4 (lane / 32) + (lane % 16) / 4 (+ 8)
+  __device__ __forceinline__ void init(int lane) {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      rows[ks] = Tile<D>::chunk_off(lane & 31, D < 16 ? 0 : 2 * ks + half);
+    const int i = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      int c = db * 32 + (lane & 16) + 4 * (i & 3);
+      if (c >= D) c &= (D - 1);  // channels >= D only feed result rows that are never used
+      const int x = 4 * half + (i >> 2);
+      tr[db][0] = Tile<D>::quad_off(x, c);
+      tr[db][1] = Tile<D>::quad_off(x + 8, c);
+    }
+  }
+  // A operand: rows = positions x0 + 0..31 (x0 a multiple of 16), k = channels of step ks.
+  // `tile` is the LDS byte address of the staged tile.
+  __device__ __forceinline__ u32x4 rows_operand(uint32_t tile, int x0, int ks, int lane) const {
+    const u32x4 v = lds_load16(tile + rows[ks] + x0 * (2 * D));
+    if (D < 16 && (lane >> 5)) return u32x4{0u, 0u, 0u, 0u};
+    return v;
+  }
+  // A operand: rows = channels 32 db + (lane & 31), k = 16 positions p0 + 16 t + the
+  // permutation of MFMA accumulator registers 8t..8t+7 (ds_read_b64_tr_b16), so
+  // those registers of a tile whose rows are the positions p0.., packed to bf16,
+  // are the matching B operand.
+  __device__ __forceinline__ u32x4 tr_operand(uint32_t tile, int db, int p0, int t) const {
+    const uint32_t base = tile + (p0 + 16 * t) * (2 * D);
+    const u32x2 lo = lds_load_tr(base + tr[db][0]);
+    const u32x2 hi = lds_load_tr(base + tr[db][1]);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
+// Direct copies of one pipeline stage: NT staged tiles, tile i holding positions
+// x0 .. x0 + kBlk - 1 of the (row, head) slab that starts at byte pointer base[i].
+// The stage's 16-byte chunks are spread over the workgroup's 256 threads in LDS
+// order.  Full blocks use the uniform-base form; the last, partial block reads
+// positions >= n from position n - 1 (values that are never used with a nonzero
+// weight).
+template <int D, int NT>
+struct Stager {
+  static constexpr int CH = Tile<D>::CHUNKS;
+  static constexpr int PER_TILE = kBlk * CH;
+  static constexpr int NIT = NT * PER_TILE / 256;  // copies per thread per stage
+  static_assert(NT * PER_TILE % 256 == 0, "stage must be a multiple of 256 chunks");
+  uint32_t voff[NIT];  // byte offset of the chunk from position x0 of its slab
+  int xr[NIT];         // position of the chunk within the block
+  int cb[NIT];         // byte offset of the chunk within its position
+  uint32_t pstride;    // bytes between consecutive positions
+
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t pstride_bytes) {
+    pstride = pstride_bytes;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int within = (it * 256 + wave * 64 + lane) % PER_TILE;
+      const int x = within / CH;
+      const int p = (within % CH) ^ Tile<D>::swz(x);
+      xr[it] = x;
+      cb[it] = p * 16;
+      voff[it] = static_cast<uint32_t>(x) * pstride_bytes + p * 16;
+    }
+  }
+  // Tile index of copy `it` of `wave` (uniform; a compile-time constant when a
+  // tile spans whole multiples of the workgroup's 256 chunks).
+  template <int IT>
+  __device__ __forceinline__ static int tile_of(int wave) {
+    if constexpr (PER_TILE % 256 == 0) return IT * 256 / PER_TILE;
+    else return (IT * 256 + wave * 64) / PER_TILE;
+  }
+  template <int IT>
+  __device__ __forceinline__ void issue_one(uint32_t lds, const char* const (&base)[NT], int x0, bool full,
+                                            int n, int wave) const {
+    const int ti = tile_of<IT>(wave);
+    const char* b = base[0];
+#pragma unroll
+    for (int i = 1; i < NT; ++i)
+      if (ti == i) b = base[i];
+    const uint32_t dst = lds + (IT * 256 + wave * 64) * 16;
+    if (full) {
+      copy16_to_lds(uniform_ptr(b + static_cast<size_t>(x0) * pstride), voff[IT], dst);
+    } else {
+      const int pos = min(x0 + xr[IT], n - 1);
+      copy16_to_lds(b + static_cast<size_t>(pos) * pstride + cb[IT], dst);
+    }
+  }
+  template <int IT = 0>
+  __device__ __forceinline__ void issue(uint32_t lds, const char* const (&base)[NT], int x0, int n, int wave) const {
+    if constexpr (IT < NIT) {
+      issue_one<IT>(lds, base, x0, x0 + kBlk <= n, n, wave);
+      issue<IT + 1>(lds, base, x0, n, wave);
+    }
+  }
+};
+
+// ---------------------------------------------------------------- tiled bias
+// The pre-scaled bias sqrt(d) * bias[h][j][k] in fp32, stored as 32 x 32 tiles in
+// the MFMA accumulator order, so that one accumulator tile is four fully
+// coalesced 1 KB loads.  Orientation 0 ("query lanes"): accumulator rows are
+// keys and lanes are queries (S^T tiles).  Orientation 1 ("key lanes"): rows are
+// queries, lanes are keys (S tiles).  Tile (qt, kt) of head h starts at float
+// ((h * nt + qt) * nt + kt) * 1024; inside it, register v = 4 g + e of lane l is
+// float g * 256 + 4 l + e.  Keys >= N hold -inf, queries >= N hold 0.
+__device__ __forceinline__ int64_t bias_tile_offset(int h, int qt, int kt, int nt) {
+  return ((static_cast<int64_t>(h) * nt + qt) * nt + kt) * 1024;
+}
+
+__device__ __forceinline__ f32x16 load_bias_tile(const float* __restrict__ tile, int lane) {
+  f32x16 c;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(tile + g * 256 + 4 * lane);
+    c[4 * g + 0] = x[0];
+    c[4 * g + 1] = x[1];
+    c[4 * g + 2] = x[2];
+    c[4 * g + 3] = x[3];
+  }
+  return c;
+}
+
+}  // namespace pipe
+
+// Number of 32-wide tiles per axis of the tiled bias (positions padded to kBlk).
+inline int bias_tiles(int n) { return (n + pipe::kBlk - 1) / pipe::kBlk * (pipe::kBlk / 32); }
+size_t tiled_bias_bytes(const Problem& p);
+// Writes the tiled, sqrt(d)-scaled fp32 bias (orientation 0 or 1, see above).
+hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out, int orientation, hipStream_t s);
+
+}  // namespace evo

@@ -5,10 +5,12 @@ Tolerances (from the statement of the target for this operator):
   fp32 mode: every output within 1e-4 max abs of the fp64 oracle.
   bf16 mode: O within 2e-2 max abs; each gradient within 5e-2 of the oracle,
              measured as max|g - g_ref| / max|g_ref| ("relative to max norm");
-             lse within 2.5e-3 max abs.  The softmax normaliser is the sum of
-             the bf16-rounded probabilities that also weight V, and each of
-             those carries a relative rounding error of at most 2^-9, so
-             |lse - lse_exact| <= 2^-9 (~1.95e-3) plus fp32 accumulation noise.
+             lse within 4e-3 max abs.  The softmax normaliser is the sum of
+             the bf16-rounded probabilities that also weight V (so O is an exact
+             convex combination of V rows).  Round-to-nearest-even to bf16 (8
+             significant bits) has relative error at most 2^-8, so the sum, and
+             hence exp(lse), is off by a factor within 1 +- 2^-8:
+             |lse - lse_exact| <= 2^-8 (3.9e-3) plus fp32 noise.
 """
 import numpy as np
 import torch
@@ -18,7 +20,7 @@ import oracle
 FP32_ATOL = 1e-4
 BF16_O_ATOL = 2e-2
 BF16_GRAD_REL = 5e-2
-BF16_LSE_ATOL = 2.5e-3
+BF16_LSE_ATOL = 4e-3
 
 
 def to_np(t):

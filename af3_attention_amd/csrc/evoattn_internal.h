@@ -42,6 +42,8 @@ struct BwdArgs {
   void* dv;
   float* dbias;       // [H,N,N] or nullptr
   float* delta;       // workspace [R,H,N]: sum_c dout*o per softmax row
+  void* qaug;         // MFMA path workspace [R,H,N] x 16 B: per-query split operands (lse, delta)
+  void* kaug;         // MFMA path workspace [R,N] x 16 B: per-key split operands (mask)
   float* scratch;     // further workspace (path specific)
   size_t scratch_bytes;
 };
@@ -71,6 +73,11 @@ size_t fwd_mfma_workspace_bytes(const Problem& p);
 size_t bwd_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_fwd_mfma(const Problem& p, const FwdArgs& a, void* ws, hipStream_t s);
 hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& a, void* ws, hipStream_t s);
+
+// dBias partial sums over fixed row groups (kernels_bwd_dbias.hip): out[g][h][j][k].
+int dbias_pipe_groups(const Problem& p);
+hipError_t launch_dbias_pipe(const Problem& p, const BwdArgs& a, const float* bias_k, int groups, float* out,
+                             hipStream_t s);
 
 // bf16 storage conversions (round to nearest even; NaN stays NaN).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

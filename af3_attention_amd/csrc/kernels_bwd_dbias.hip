@@ -1,0 +1,226 @@
+// dBias of pair-biased 3D attention (bf16 MFMA, gfx950).
+//
+// The bias is shared by every attention row (MegaFold pages, gist.science
+// technical summary, Methodik section 1 "EvoFlash-3D": an additively broadcast
+// pair bias), so its gradient is a sum over rows:
+//   dBias[h,j,k] = sum_r dS[r,h,j,k],  dS = P * (dP - D),
+// with P recomputed from the saved logsumexp.  To make the sum deterministic,
+// each workgroup owns a 128 x 128 (query x key) tile of one head and walks a
+// fixed group of rows in increasing order, adding dS into registers; groups write
+// partial sums that a last pass adds in increasing group order.
+//
+// Per row the workgroup stages Q, dO (its 128 queries), K, V (its 128 keys) and
+// the row's split lse, D and mask operands in LDS with direct copies, through a ring of four
+// stages (two at d = 64; copies run that many rows ahead minus one).  The 8 waves split the tile into 4 key tiles x 2
+// query halves; a wave owns 32 keys and two 32-query tiles:
+//   S  = Q K^T + sqrt(d) bias + sqrt(d) (mask - lse)   (bias: accumulator input;
+//        mask and lse: one extra MFMA step on split-bf16 operands)
+//   dP = dO V^T - D                                   (D: one extra MFMA step)
+//   acc += exp2(S log2(e)/sqrt(d)) * dP               (one mul, one exp2, one FMA)
+
+#include <algorithm>
+#include <type_traits>
+
+#include "pipe_common.h"
+
+namespace evo {
+namespace {
+
+using namespace mfma;
+using namespace pipe;
+
+constexpr int kDbT = 128;      // tile edge (queries and keys)
+constexpr int kDbThreads = 512;  // 8 waves: 4 key tiles x 2 query halves
+// LDS ring of rows (copies run db_stages - 1 rows ahead): four stages of 34.5 KB
+// up to d = 32, two of 66 KB at d = 64.
+template <int D>
+constexpr int db_stages() { return D >= 64 ? 2 : 4; }
+
+template <int D>
+__global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, BwdArgs a,
+                                                                   const float* __restrict__ bias_k, int nt,
+                                                                   int groups, float* __restrict__ out) {
+  constexpr int TB = Tile<D, kDbT>::BYTES;
+  constexpr int STATS = 2 * kDbT * 16;  // query-side (lse, D) and key-side (mask) split operands
+  constexpr int STAGE = 4 * TB + STATS;
+  constexpr int NS = db_stages<D>();
+  constexpr int DUMMY = NS * STAGE;  // 1 KB target of dummy copies
+  constexpr int KS = Shape<D>::KS;
+  using St = Stager<D, 2, kDbT, kDbThreads>;
+  constexpr int NROW = 2 * St::NIT + 1;  // copies per thread per row: Q/dO, K/V, one operand piece
+  __shared__ __align__(16) char lds[NS * STAGE + 1024];
+
+  const int nb = (p.N + kDbT - 1) / kDbT;
+  int blk = xcd_logical_block(blockIdx.x, nb * nb * groups * p.H);
+  const int kb = blk % nb;
+  blk /= nb;
+  const int qb = blk % nb;
+  blk /= nb;
+  const int g = blk % groups;
+  const int h = blk / groups;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int wk = wave & 3, wq = wave >> 2;  // key tile, query half of this wave
+  const int q0 = qb * kDbT, k0 = kb * kDbT;
+
+  const int rows_per = (p.R + groups - 1) / groups;
+  const int r_begin = g * rows_per;
+  const int r_end = min(p.R, r_begin + rows_per);
+
+  const float sd = sqrtf(static_cast<float>(D));
+  const float c1 = kLog2e / sd;
+  const uint32_t pstride = static_cast<uint32_t>(p.pos_stride * p.H * D * 2);
+  const uint32_t lds0 = lds_addr(lds);
+  St stager;
+  stager.init(wave, lane, pstride);
+  TileReads<D> rd;
+  rd.init(lane);
+
+  // sqrt(d) * bias of this wave's 32 keys and two 32-query tiles: constant over
+  // the rows, so it is loaded once.
+  f32x16 bias[2], acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bias[t] = load_bias_tile(bias_k + bias_tile_offset(h, qb * 4 + 2 * wq + t, kb * 4 + wk, nt), lane);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  }
+  const u32x4 dp_key = key_aug_unit(lane);
+  const uint16_t* const qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* const dop = static_cast<const uint16_t*>(a.dout);
+  const uint16_t* const kp = static_cast<const uint16_t*>(a.k);
+  const uint16_t* const vp = static_cast<const uint16_t*>(a.v);
+
+  // Copies of row r into stage s: Q, dO (queries q0..), K, V (keys k0..), and one
+  // 64-entry piece of the split operands for each of waves 0..3.
+  auto issue_row = [&](int r, auto stage_c) {
+    constexpr int s = decltype(stage_c)::value;
+    const uint32_t st = lds0 + s * STAGE;
+    const int64_t rh = row_head_offset(p, r, h);
+    const char* qd[2] = {uniform_ptr(reinterpret_cast<const char*>(qp + rh)),
+                         uniform_ptr(reinterpret_cast<const char*>(dop + rh))};
+    const char* kv[2] = {uniform_ptr(reinterpret_cast<const char*>(kp + rh)),
+                         uniform_ptr(reinterpret_cast<const char*>(vp + rh))};
+    stager.issue(st, qd, q0, p.N, wave, lds0 + DUMMY);
+    stager.issue(st + 2 * TB, kv, k0, p.N, wave, lds0 + DUMMY);
+    const int64_t rhn = (static_cast<int64_t>(r) * p.H + h) * p.N;
+    const int piece = wave & 1;
+    if (wave < 2) {
+      copy_rows16(static_cast<const u32x4*>(a.qaug) + rhn, q0 + 64 * piece, p.N, st + 4 * TB + 1024 * piece, lane);
+    } else if (wave < 4) {
+      copy_rows16(static_cast<const u32x4*>(a.kaug) + static_cast<int64_t>(r) * p.N, k0 + 64 * piece, p.N,
+                  st + 4 * TB + kDbT * 16 + 1024 * piece, lane);
+    } else {  // keep one operand copy per wave and row, so that waits can count them
+      copy16_to_lds(uniform_ptr(a.qaug), 0u, lds0 + DUMMY);
+    }
+  };
+
+  auto step = [&](int r, auto stage_c) {
+    constexpr int s = decltype(stage_c)::value;
+    // Row r was issued NS - 1 rows ago; up to NS - 2 later rows came after it.
+    const int later = min(NS - 2, r_end - 1 - r);
+    if (later >= 2)
+      wait_vmcnt<2 * NROW>();
+    else if (later == 1)
+      wait_vmcnt<NROW>();
+    else
+      wait_vmcnt<0>();
+    barrier();
+    if (r + NS - 1 < r_end) issue_row(r + NS - 1, std::integral_constant<int, (s + NS - 1) % NS>());
+    const uint32_t st = lds0 + s * STAGE;
+    const uint32_t tq = st, tdo = st + TB, tk = st + 2 * TB, tv = st + 3 * TB;
+    const uint32_t stats = st + 4 * TB;
+    const int kl = wk * 32 + (lane & 31);  // this lane's key within the tile
+
+    u32x4 kop[KS], vop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kop[ks] = rd.rows_operand(tk, wk * 32, ks, lane);
+      vop[ks] = rd.rows_operand(tv, wk * 32, ks, lane);
+    }
+    u32x4 s_key = lds_load16(stats + kDbT * 16 + kl * 16);
+    if (lane >> 5) s_key = u32x4{0u, 0u, 0u, 0u};
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int x0 = (2 * wq + t) * 32;      // first query of this tile within the block
+      const int jl = x0 + (lane & 31);       // this lane's query (as an A-operand row)
+      const u32x4 qa = lds_load16(stats + jl * 16);
+      const u32x4 s_q = q0 + jl < p.N ? u32x4{qa[0], qa[1], kBf16One | (kBf16One << 16), 0u} : dead_query_aug();
+      const u32x4 dp_q = {qa[2], qa[3], 0u, 0u};
+      f32x16 sacc = mma(rd.rows_operand(tq, x0, 0, lane), kop[0], bias[t]);
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tq, x0, ks, lane), kop[ks], sacc);
+      sacc = mma(s_q, s_key, sacc);
+      f32x16 dp = mma(rd.rows_operand(tdo, x0, 0, lane), vop[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tdo, x0, ks, lane), vop[ks], dp);
+      dp = mma(dp_q, dp_key, dp);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][e] = __builtin_fmaf(fast_exp2(sacc[e] * c1), dp[e], acc[t][e]);
+    }
+  };
+
+  // Prologue: rows r_begin .. r_begin + NS - 2 into stages 0 .. NS - 2.
+  if (r_begin < r_end) issue_row(r_begin, std::integral_constant<int, 0>());
+  if constexpr (NS > 2) {
+    if (r_begin + 1 < r_end) issue_row(r_begin + 1, std::integral_constant<int, 1>());
+    if (r_begin + 2 < r_end) issue_row(r_begin + 2, std::integral_constant<int, 2 % NS>());
+  }
+  for (int r = r_begin; r < r_end; r += NS) {
+    step(r, std::integral_constant<int, 0>());
+    if (r + 1 < r_end) step(r + 1, std::integral_constant<int, 1>());
+    if constexpr (NS > 2) {
+      if (r + 2 < r_end) step(r + 2, std::integral_constant<int, 2 % NS>());
+      if (r + 3 < r_end) step(r + 3, std::integral_constant<int, 3 % NS>());
+    }
+  }
+
+  // Partial sums of this group: out[g][h][j][k].
+  const int key = k0 + wk * 32 + (lane & 31);
+  if (key >= p.N) return;
+  float* dst = out + (static_cast<int64_t>(g) * p.H + h) * p.N * p.N + key;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = q0 + (2 * wq + t) * 32 + acc_row(v, lane);
+      if (j < p.N) dst[static_cast<int64_t>(j) * p.N] = acc[t][v];
+    }
+}
+
+}  // namespace
+
+int dbias_pipe_groups(const Problem& p) {
+  const int nb = (p.N + kDbT - 1) / kDbT;
+  const int64_t tiles = static_cast<int64_t>(p.H) * nb * nb;
+  // About one full round of resident workgroups (one per CU on 256 CUs).
+  int64_t g = std::max<int64_t>(1, 256 / tiles);
+  g = std::min<int64_t>(g, p.R);
+  return static_cast<int>(g);
+}
+
+hipError_t launch_dbias_pipe(const Problem& p, const BwdArgs& a, const float* bias_k, int groups, float* out,
+                             hipStream_t s) {
+  const int nb = (p.N + kDbT - 1) / kDbT;
+  const int64_t blocks = static_cast<int64_t>(nb) * nb * groups * p.H;
+  const int nt = bias_tiles(p.N);
+  KernelTimer timer("bwd_dbias_mfma", s);
+  switch (p.D) {
+    case 8:
+      hipLaunchKernelGGL((dbias_pipe_kernel<8>), dim3(blocks), dim3(kDbThreads), 0, s, p, a, bias_k, nt, groups, out);
+      break;
+    case 16:
+      hipLaunchKernelGGL((dbias_pipe_kernel<16>), dim3(blocks), dim3(kDbThreads), 0, s, p, a, bias_k, nt, groups, out);
+      break;
+    case 32:
+      hipLaunchKernelGGL((dbias_pipe_kernel<32>), dim3(blocks), dim3(kDbThreads), 0, s, p, a, bias_k, nt, groups, out);
+      break;
+    case 64:
+      hipLaunchKernelGGL((dbias_pipe_kernel<64>), dim3(blocks), dim3(kDbThreads), 0, s, p, a, bias_k, nt, groups, out);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace evo

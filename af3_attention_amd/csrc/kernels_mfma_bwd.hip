@@ -25,7 +25,7 @@
 
 #include <algorithm>
 
-#include "mfma_common.h"
+#include "pipe_common.h"
 
 namespace evo {
 namespace {
@@ -332,120 +332,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(Problem p, BwdArgs 
   store_dT<D>(static_cast<uint16_t*>(a.dq) + elem_offset(p, r, j, h), dq_acc, 1.f / sd, half);
 }
 
-// ------------------------------------------------------------------ dBias
-// Workgroup = (head, 64-query block, 128-key block, row group); wave w owns keys
-// 32w..32w+31 of the block and both 32-query tiles.  Rows of the group are
-// visited in increasing order and dS is summed in registers.
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dbias_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_t,
-                                                                int np, int row_groups, float* __restrict__ out) {
-  using S = Shape<D>;
-  __shared__ __align__(16) uint16_t q_rows[2][kStep * S::ROW];
-  __shared__ __align__(16) uint16_t do_rows[2][kStep * S::ROW];
-  __shared__ __align__(16) float nlse_lds[2][kStep];
-  __shared__ __align__(16) float ndel_lds[2][kStep];
-
-  const int nkb = (p.N + 127) / 128;
-  const int nqb = (p.N + kStep - 1) / kStep;
-  int blk = blockIdx.x;
-  const int kb = blk % nkb;
-  blk /= nkb;
-  const int qb = blk % nqb;
-  blk /= nqb;
-  const int h = blk % p.H;
-  const int g = blk / p.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int key = kb * 128 + wave * 32 + col;  // < np
-  const int q0 = qb * kStep;
-  const bool valid = key < p.N;
-
-  const int rows_per = (p.R + row_groups - 1) / row_groups;
-  const int r_begin = g * rows_per;
-  const int r_end = min(p.R, r_begin + rows_per);
-
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* k = static_cast<const uint16_t*>(a.k);
-  const uint16_t* v = static_cast<const uint16_t*>(a.v);
-  const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
-  const float sd = sqrtf(static_cast<float>(D));
-  const float c1 = kLog2e / sd;
-
-  const float* brow = bias_t + (static_cast<int64_t>(h) * np + key) * np + q0;
-  const f32x16 b0 = load_acc_rows(brow, half);
-  const f32x16 b1 = load_acc_rows(brow + 32, half);
-
-  f32x16 acc[2];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
-
-  const int64_t pstep = pos_step(p);
-  Stage<D> qst, dost;
-  qst.init(p);
-  dost.init(p);
-  StatStage stst;
-  u32x4 knext[S::KS], vnext[S::KS];
-  float mnext = 0.f;
-  // Row r's query block q0 starts at element (r, q0, h, 0).
-  auto fetch = [&](int r) {
-    const int64_t base = row_head_offset(p, r, h) + q0 * pstep;
-    qst.load(q + base, q0, p.N);
-    dost.load(dout + base, q0, p.N);
-    stst.load(p, a, r, h, q0);
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      knext[ks] = global_operand<D>(p, k, r, key, h, ks, half);
-      vnext[ks] = global_operand<D>(p, v, r, key, h, ks, half);
-    }
-    mnext = (a.mask && valid) ? a.mask[static_cast<int64_t>(r) * p.N + key] : 0.f;
-  };
-  if (r_begin < r_end) fetch(r_begin);
-
-  int buf = 0;
-  for (int r = r_begin; r < r_end; ++r) {
-    qst.store(q_rows[buf], nullptr, S::ROW, q0, p.N);
-    dost.store(do_rows[buf], nullptr, S::ROW, q0, p.N);
-    stst.store(nlse_lds[buf], ndel_lds[buf]);
-    u32x4 kreg[S::KS], vreg[S::KS];
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      kreg[ks] = knext[ks];
-      vreg[ks] = vnext[ks];
-    }
-    const float mk = mnext;
-    lds_barrier();
-    const int cb = buf;
-    buf ^= 1;
-    if (r + 1 < r_end) fetch(r + 1);
-    const bool wave_live = __ballot(valid && mk != -INFINITY) != 0;
-    if (!wave_live) continue;
-    const bool any_mask = __ballot(valid && mk != 0.f) != 0;
-    const float mk_s = sd * mk;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      f32x16 c = qt == 0 ? b0 : b1;
-      if (any_mask) c += mk_s;
-      f32x16 s = mma(rows_operand<D>(q_rows[cb], 32 * qt, 0, col, half), kreg[0], c);
-#pragma unroll
-      for (int ks = 1; ks < S::KS; ++ks) s = mma(rows_operand<D>(q_rows[cb], 32 * qt, ks, col, half), kreg[ks], s);
-      const f32x16 nl = load_acc_rows(&nlse_lds[cb][32 * qt], half);
-      f32x16 dp = load_acc_rows(&ndel_lds[cb][32 * qt], half);
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) dp = mma(rows_operand<D>(do_rows[cb], 32 * qt, ks, col, half), vreg[ks], dp);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[qt][i] += fast_exp2(__builtin_fmaf(s[i], c1, nl[i])) * dp[i];
-    }
-  }
-  if (!valid) return;
-  float* dst = out + static_cast<int64_t>(g) * p.H * p.N * p.N + static_cast<int64_t>(h) * p.N * p.N + key;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int jq = q0 + 32 * qt + acc_row(i, lane);
-      if (jq < p.N) dst[static_cast<int64_t>(jq) * p.N] = acc[qt][i];
-    }
-}
-
 // dbias[i] = sum over groups g = 0, 1, ... of part[g][i], in increasing g.
 __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restrict__ part, int groups, int64_t n,
                                                            float* __restrict__ dbias) {
@@ -457,16 +343,23 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restri
   }
 }
 
-// delta[r,h,j] = sum_c dout[r,j,h,c] * o[r,j,h,c]; one lane per softmax row.
+// Per-row terms of the backward, one thread per (r, j, h) in memory order (so a
+// wave reads contiguous 2*d-byte pieces of O and dO):
+//   delta[r,h,j] = sum_c dout[r,j,h,c] o[r,j,h,c]
+//   qaug[r,h,j]  = the query-side split operands of -sqrt(d) lse and -delta
+//   kaug[r,j]    = the key-side split operands of sqrt(d) mask (threads with h = 0)
+// (layouts of the operands: pipe_common.h).
 template <int D>
-__global__ __launch_bounds__(256) void delta_bf16_kernel(Problem p, BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_rowterms_kernel(Problem p, BwdArgs a) {
+  using namespace pipe;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(p.R) * p.H * p.N;
   if (idx >= total) return;
-  const int j = static_cast<int>(idx % p.N);
-  const int h = static_cast<int>((idx / p.N) % p.H);
-  const int r = static_cast<int>(idx / (static_cast<int64_t>(p.N) * p.H));
-  const int64_t off = elem_offset(p, r, j, h);
+  const int h = static_cast<int>(idx % p.H);
+  const int64_t pr = idx / p.H;  // (r, j) or (j, r) in memory order
+  const int r = static_cast<int>(p.transpose ? pr % p.R : pr / p.N);
+  const int j = static_cast<int>(p.transpose ? pr / p.R : pr % p.N);
+  const int64_t off = idx * D;
   const u32x4* o = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.o) + off);
   const u32x4* d = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dout) + off);
   float s = 0.f;
@@ -479,24 +372,29 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(Problem p, BwdArgs a) {
       s += __uint_as_float(x[i] & 0xffff0000u) * __uint_as_float(y[i] & 0xffff0000u);
     }
   }
-  a.delta[idx] = s;
-}
-
-int dbias_row_groups(const Problem& p) {
-  const int64_t tiles = static_cast<int64_t>(p.H) * ((p.N + kStep - 1) / kStep) * ((p.N + 127) / 128);
-  int64_t g = (2048 + tiles - 1) / tiles;  // aim for >= 2048 workgroups
-  g = std::max<int64_t>(1, std::min<int64_t>(g, std::min<int64_t>(16, p.R)));
-  return static_cast<int>(g);
+  const int64_t rhj = (static_cast<int64_t>(r) * p.H + h) * p.N + j;
+  a.delta[rhj] = s;
+  const float sd = sqrtf(static_cast<float>(D));
+  const Split3 na = split3(-lse_term(a.lse[rhj], sd, true));
+  const Split3 nd = split3(-s);
+  reinterpret_cast<u32x4*>(a.qaug)[rhj] =
+      u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), nd.hi | (nd.mid << 16), nd.lo};
+  if (h == 0) {
+    const float m = a.mask ? a.mask[static_cast<int64_t>(r) * p.N + j] : 0.f;
+    const Split3 sm = split3(fmaxf(sd * m, -kHuge));
+    reinterpret_cast<u32x4*>(a.kaug)[static_cast<int64_t>(r) * p.N + j] =
+        u32x4{kBf16One | (kBf16One << 16), kBf16One | (sm.hi << 16), sm.mid | (sm.lo << 16), 0u};
+  }
 }
 
 template <int D>
-hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_f, float* bias_t, int np,
+hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_f, float* bias_t, float* bias_k, int np,
                              float* dbias_part, int groups, hipStream_t s) {
   hipError_t e;
   {
     const int64_t rows_total = static_cast<int64_t>(p.R) * p.H * p.N;
-    KernelTimer timer("bwd_delta", s);
-    hipLaunchKernelGGL((delta_bf16_kernel<D>), dim3(static_cast<unsigned>((rows_total + 255) / 256)), dim3(256), 0,
+    KernelTimer timer("bwd_rowterms", s);
+    hipLaunchKernelGGL((bwd_rowterms_kernel<D>), dim3(static_cast<unsigned>((rows_total + 255) / 256)), dim3(256), 0,
                        s, p, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -517,15 +415,9 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_f, 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.dbias) {
-    const int64_t blocks =
-        static_cast<int64_t>((p.N + 127) / 128) * ((p.N + kStep - 1) / kStep) * p.H * groups;
+    if ((e = launch_bias_tiles(p, a.bias, bias_k, 1, s)) != hipSuccess) return e;
     float* target = groups == 1 ? a.dbias : dbias_part;
-    {
-      KernelTimer timer("bwd_dbias_mfma", s);
-      hipLaunchKernelGGL((bwd_dbias_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p, a,
-                         bias_t, np, groups, target);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    if ((e = launch_dbias_pipe(p, a, bias_k, groups, target, s)) != hipSuccess) return e;
     if (groups > 1) {
       const int64_t n = static_cast<int64_t>(p.H) * p.N * p.N;
       const int rb = static_cast<int>(std::min<int64_t>((n + 255) / 256, 4096));
@@ -541,33 +433,42 @@ size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-// Workspace: delta [R,H,N] | bias_f [H,np,np] | bias_t [H,np,np] | dbias partials [G,H,N,N].
+// Workspace: delta [R,H,N] | qaug [R,H,N] x 16 B | kaug [R,N] x 16 B |
+// bias_f, bias_t [H,np,np] | tiled bias (key lanes) | dbias partials [G,H,N,N].
 size_t bwd_mfma_workspace_bytes(const Problem& p) {
   const size_t np = static_cast<size_t>(bias_pad(p.N));
-  const int groups = dbias_row_groups(p);
-  const size_t delta = align_up(static_cast<size_t>(p.R) * p.H * p.N * sizeof(float));
+  const int groups = dbias_pipe_groups(p);
+  const size_t delta = align_up(static_cast<size_t>(p.R) * p.H * p.N * sizeof(float)) +
+                       align_up(static_cast<size_t>(p.R) * p.H * p.N * 16) + align_up(static_cast<size_t>(p.R) * p.N * 16);
   const size_t bias = align_up(static_cast<size_t>(p.H) * np * np * sizeof(float));
+  const size_t tiled = align_up(tiled_bias_bytes(p));
   const size_t part = groups > 1 ? align_up(static_cast<size_t>(groups) * p.H * p.N * p.N * sizeof(float)) : 0;
-  return delta + 2 * bias + part;
+  return delta + 2 * bias + tiled + part;
 }
 
 hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& args, void* ws, hipStream_t s) {
   const size_t np = static_cast<size_t>(bias_pad(p.N));
-  const int groups = dbias_row_groups(p);
+  const int groups = dbias_pipe_groups(p);
   char* base = static_cast<char*>(ws);
   BwdArgs a = args;
   a.delta = reinterpret_cast<float*>(base);
   base += align_up(static_cast<size_t>(p.R) * p.H * p.N * sizeof(float));
+  a.qaug = base;
+  base += align_up(static_cast<size_t>(p.R) * p.H * p.N * 16);
+  a.kaug = base;
+  base += align_up(static_cast<size_t>(p.R) * p.N * 16);
   float* bias_f = reinterpret_cast<float*>(base);
   base += align_up(static_cast<size_t>(p.H) * np * np * sizeof(float));
   float* bias_t = reinterpret_cast<float*>(base);
   base += align_up(static_cast<size_t>(p.H) * np * np * sizeof(float));
+  float* bias_k = reinterpret_cast<float*>(base);
+  base += align_up(tiled_bias_bytes(p));
   float* part = reinterpret_cast<float*>(base);
   switch (p.D) {
-    case 8: return bwd_mfma_dispatch<8>(p, a, bias_f, bias_t, static_cast<int>(np), part, groups, s);
-    case 16: return bwd_mfma_dispatch<16>(p, a, bias_f, bias_t, static_cast<int>(np), part, groups, s);
-    case 32: return bwd_mfma_dispatch<32>(p, a, bias_f, bias_t, static_cast<int>(np), part, groups, s);
-    case 64: return bwd_mfma_dispatch<64>(p, a, bias_f, bias_t, static_cast<int>(np), part, groups, s);
+    case 8: return bwd_mfma_dispatch<8>(p, a, bias_f, bias_t, bias_k, static_cast<int>(np), part, groups, s);
+    case 16: return bwd_mfma_dispatch<16>(p, a, bias_f, bias_t, bias_k, static_cast<int>(np), part, groups, s);
+    case 32: return bwd_mfma_dispatch<32>(p, a, bias_f, bias_t, bias_k, static_cast<int>(np), part, groups, s);
+    case 64: return bwd_mfma_dispatch<64>(p, a, bias_f, bias_t, bias_k, static_cast<int>(np), part, groups, s);
     default: return hipErrorInvalidValue;
   }
 }

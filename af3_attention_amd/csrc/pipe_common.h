@@ -123,10 +123,10 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
 // distinct LDS banks.
 constexpr int kBlk = 64;  // positions per pipeline stage
 
-template <int D>
+template <int D, int POS = kBlk>
 struct Tile {
   static constexpr int CHUNKS = D / 8;            // 16-byte chunks per position
-  static constexpr int BYTES = kBlk * D * 2;      // bytes per staged tile
+  static constexpr int BYTES = POS * D * 2;       // bytes per staged tile of POS positions
   static constexpr int ROWS_PER_256B = 128 / D;   // positions per 256 bytes
   __device__ __forceinline__ static int swz(int x) {
     return CHUNKS > 1 ? (x / ROWS_PER_256B) & (CHUNKS - 1) : 0;
@@ -183,17 +183,20 @@ struct TileReads {
 };
 
 // Direct copies of one pipeline stage: NT staged tiles, tile i holding positions
-// x0 .. x0 + kBlk - 1 of the (row, head) slab that starts at byte pointer base[i].
-// The stage's 16-byte chunks are spread over the workgroup's 256 threads in LDS
-// order.  Full blocks use the uniform-base form; the last, partial block reads
+// x0 .. x0 + POS - 1 of the (row, head) slab that starts at byte pointer base[i].
+// The stage's 16-byte chunks are spread over the workgroup's THREADS threads in
+// LDS order.  Full blocks use the uniform-base form; the last, partial block reads
 // positions >= n from position n - 1 (values that are never used with a nonzero
-// weight).
-template <int D, int NT>
+// weight).  Every wave issues exactly NIT copies per stage, so that waits can
+// count them: a wave without chunks left issues a dummy copy into the 1 KB
+// `dummy` LDS area (contents never read).
+template <int D, int NT, int POS = kBlk, int THREADS = 256>
 struct Stager {
   static constexpr int CH = Tile<D>::CHUNKS;
-  static constexpr int PER_TILE = kBlk * CH;
-  static constexpr int NIT = NT * PER_TILE / 256;  // copies per thread per stage
-  static_assert(NT * PER_TILE % 256 == 0, "stage must be a multiple of 256 chunks");
+  static constexpr int PER_TILE = POS * CH;
+  static constexpr int TOTAL = NT * PER_TILE;                  // chunks per stage
+  static constexpr int NIT = (TOTAL + THREADS - 1) / THREADS;  // copies per thread per stage
+  static_assert(TOTAL % 64 == 0, "stage must be a multiple of 64 chunks");
   uint32_t voff[NIT];  // byte offset of the chunk from position x0 of its slab
   int xr[NIT];         // position of the chunk within the block
   int cb[NIT];         // byte offset of the chunk within its position
@@ -203,7 +206,7 @@ struct Stager {
     pstride = pstride_bytes;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int within = (it * 256 + wave * 64 + lane) % PER_TILE;
+      const int within = (it * THREADS + wave * 64 + lane) % PER_TILE;
       const int x = within / CH;
       const int p = (within % CH) ^ Tile<D>::swz(x);
       xr[it] = x;
@@ -212,21 +215,25 @@ struct Stager {
     }
   }
   // Tile index of copy `it` of `wave` (uniform; a compile-time constant when a
-  // tile spans whole multiples of the workgroup's 256 chunks).
+  // tile spans whole multiples of the workgroup's chunks).
   template <int IT>
   __device__ __forceinline__ static int tile_of(int wave) {
-    if constexpr (PER_TILE % 256 == 0) return IT * 256 / PER_TILE;
-    else return (IT * 256 + wave * 64) / PER_TILE;
+    if constexpr (PER_TILE % THREADS == 0) return IT * THREADS / PER_TILE;
+    else return min((IT * THREADS + wave * 64) / PER_TILE, NT - 1);
   }
   template <int IT>
   __device__ __forceinline__ void issue_one(uint32_t lds, const char* const (&base)[NT], int x0, bool full,
-                                            int n, int wave) const {
+                                            int n, int wave, uint32_t dummy) const {
+    if (TOTAL % THREADS != 0 && IT * THREADS + wave * 64 >= TOTAL) {
+      copy16_to_lds(uniform_ptr(base[0]), 0u, dummy);
+      return;
+    }
     const int ti = tile_of<IT>(wave);
     const char* b = base[0];
 #pragma unroll
     for (int i = 1; i < NT; ++i)
       if (ti == i) b = base[i];
-    const uint32_t dst = lds + (IT * 256 + wave * 64) * 16;
+    const uint32_t dst = lds + (IT * THREADS + wave * 64) * 16;
     if (full) {
       copy16_to_lds(uniform_ptr(b + static_cast<size_t>(x0) * pstride), voff[IT], dst);
     } else {
@@ -235,10 +242,11 @@ struct Stager {
     }
   }
   template <int IT = 0>
-  __device__ __forceinline__ void issue(uint32_t lds, const char* const (&base)[NT], int x0, int n, int wave) const {
+  __device__ __forceinline__ void issue(uint32_t lds, const char* const (&base)[NT], int x0, int n, int wave,
+                                        uint32_t dummy = 0) const {
     if constexpr (IT < NIT) {
-      issue_one<IT>(lds, base, x0, x0 + kBlk <= n, n, wave);
-      issue<IT + 1>(lds, base, x0, n, wave);
+      issue_one<IT>(lds, base, x0, x0 + POS <= n, n, wave, dummy);
+      issue<IT + 1>(lds, base, x0, n, wave, dummy);
     }
   }
 };
@@ -270,10 +278,96 @@ __device__ __forceinline__ f32x16 load_bias_tile(const float* __restrict__ tile,
 
 }  // namespace pipe
 
-// Number of 32-wide tiles per axis of the tiled bias (positions padded to kBlk).
-inline int bias_tiles(int n) { return (n + pipe::kBlk - 1) / pipe::kBlk * (pipe::kBlk / 32); }
+// Number of 32-wide tiles per axis of the tiled bias (positions padded to 128).
+inline int bias_tiles(int n) { return (n + 127) / 128 * 4; }
 size_t tiled_bias_bytes(const Problem& p);
 // Writes the tiled, sqrt(d)-scaled fp32 bias (orientation 0 or 1, see above).
 hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out, int orientation, hipStream_t s);
 
+}  // namespace evo
+
+namespace evo {
+namespace pipe {
+
+// ---------------------------------------------------------------- per-row terms
+// Per-row terms (the key mask, the logsumexp, the softmax Jacobian's D) enter the
+// MFMA accumulators through one extra 16-deep step instead of vector ALU work:
+// the query side and the key side each hold 8 bf16 values in the k slots 0..7
+// (lanes 0..31; lanes 32..63 are the k slots 8..15), and their product is
+//   sum_k q_aug[k] key_aug[k].
+// The key side is zero in lanes 32..63, so the query side may hold anything
+// finite there.  A finite float x is carried exactly as the sum of three bf16
+// parts obtained by truncation: hi = top 16 bits of x, mid = top 16 bits of
+// x - hi, lo = x - hi - mid (at most 8 significant bits, so exact in bf16).
+struct Split3 {
+  uint32_t hi, mid, lo;  // bf16 bit patterns in the low 16 bits
+};
+__device__ __forceinline__ Split3 split3(float x) {
+  const uint32_t h = __float_as_uint(x) & 0xffff0000u;
+  const float r1 = x - __uint_as_float(h);
+  const uint32_t m = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(m);
+  return Split3{h >> 16, m >> 16, __float_as_uint(r2) >> 16};
+}
+
+constexpr uint32_t kBf16One = 0x3f80u;
+constexpr float kHuge = 1e30f;  // stands in for infinity in the split operands
+
+// Key side of the logits: k slots [1, 1, 1, m, m, m, 0, 0] (m = sqrt(d) * mask,
+// a masked key's -inf replaced by -1e30), zero in lanes 32..63.
+__device__ __forceinline__ u32x4 key_aug(float m_scaled, int lane) {
+  const Split3 m = split3(fmaxf(m_scaled, -kHuge));
+  const u32x4 v = {kBf16One | (kBf16One << 16), kBf16One | (m.hi << 16), m.mid | (m.lo << 16), 0u};
+  return (lane >> 5) ? u32x4{0u, 0u, 0u, 0u} : v;
+}
+// Key side of dP: [1, 1, 1, 0, 0, 0, 0, 0], zero in lanes 32..63.
+__device__ __forceinline__ u32x4 key_aug_unit(int lane) {
+  const u32x4 v = {kBf16One | (kBf16One << 16), kBf16One, 0u, 0u};
+  return (lane >> 5) ? u32x4{0u, 0u, 0u, 0u} : v;
+}
+// Query side of the logits: [-a, -a, -a, 1, 1, 1, 0, 0] (a = sqrt(d) * lse, split).
+// With key_aug this adds sqrt(d) * (mask - lse) to the logit accumulator.
+__device__ __forceinline__ u32x4 query_aug_lse(float a) {
+  const Split3 n = split3(-a);
+  return u32x4{n.hi | (n.mid << 16), n.lo | (kBf16One << 16), kBf16One | (kBf16One << 16), 0u};
+}
+// Query side of dP: [-D, -D, -D, 0, 0, 0, 0, 0]; with key_aug_unit it adds -D.
+__device__ __forceinline__ u32x4 query_aug_delta(float dlt) {
+  const Split3 n = split3(-dlt);
+  return u32x4{n.hi | (n.mid << 16), n.lo, 0u, 0u};
+}
+
+// sqrt(d) * lse as used by the query side: a query whose keys are all masked
+// (lse = -inf), or a padding query, gets a huge finite value so that every
+// probability of it is exactly 0 and no inf - inf arises.
+__device__ __forceinline__ float lse_term(float lse, float sd, bool valid) {
+  return (valid && lse != -INFINITY) ? sd * lse : kHuge;
+}
+
+// Query side of the logits for a padding query: -1e30 in the lse slots, so that
+// its probabilities are exactly 0.
+__device__ __forceinline__ u32x4 dead_query_aug() {
+  const Split3 n = split3(-kHuge);
+  return u32x4{n.hi | (n.mid << 16), n.lo | (kBf16One << 16), kBf16One | (kBf16One << 16), 0u};
+}
+
+// Direct copy of 64 consecutive 16-byte entries (one per lane) of a row vector
+// starting at entry x0; entries past n read entry n - 1.
+__device__ __forceinline__ void copy_rows16(const u32x4* row, int x0, int n, uint32_t dst, int lane) {
+  if (x0 + 64 <= n)
+    copy16_to_lds(uniform_ptr(row + x0), static_cast<uint32_t>(lane) * 16, dst);
+  else
+    copy16_to_lds(row + min(x0 + lane, n - 1), dst);
+}
+
+// Direct copy of 64 consecutive floats (one per lane) of a row vector starting at
+// element x0; elements past n read element n - 1.
+__device__ __forceinline__ void copy_row64(const float* row, int x0, int n, uint32_t dst, int lane) {
+  if (x0 + 64 <= n)
+    copy4_to_lds(uniform_ptr(row + x0), static_cast<uint32_t>(lane) * 4, dst);
+  else
+    copy4_to_lds(row + min(x0 + lane, n - 1), dst);
+}
+
+}  // namespace pipe
 }  // namespace evo

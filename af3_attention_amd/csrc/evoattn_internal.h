@@ -74,6 +74,9 @@ size_t bwd_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_fwd_mfma(const Problem& p, const FwdArgs& a, void* ws, hipStream_t s);
 hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& a, void* ws, hipStream_t s);
 
+// dK, dV (kernels_bwd_dkdv.hip); bias_k is the key-lane tiled bias.
+hipError_t launch_dkdv_pipe(const Problem& p, const BwdArgs& a, const float* bias_k, hipStream_t s);
+
 // dBias partial sums over fixed row groups (kernels_bwd_dbias.hip): out[g][h][j][k].
 int dbias_pipe_groups(const Problem& p);
 hipError_t launch_dbias_pipe(const Problem& p, const BwdArgs& a, const float* bias_k, int groups, float* out,

@@ -400,13 +400,8 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_f, 
   }
   if ((e = launch_bias_prep(p, a.bias, bias_t, np, 1, s)) != hipSuccess) return e;
   if ((e = launch_bias_prep(p, a.bias, bias_f, np, 0, s)) != hipSuccess) return e;
-  {
-    const int64_t blocks = static_cast<int64_t>((p.N + 127) / 128) * p.H * p.R;
-    KernelTimer timer("bwd_dkdv_mfma", s);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p, a, bias_t,
-                       np);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if ((e = launch_bias_tiles(p, a.bias, bias_k, 1, s)) != hipSuccess) return e;
+  if ((e = launch_dkdv_pipe(p, a, bias_k, s)) != hipSuccess) return e;
   {
     const int64_t blocks = static_cast<int64_t>((p.N + 127) / 128) * p.H * p.R;
     KernelTimer timer("bwd_dq_mfma", s);
@@ -415,7 +410,6 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_f, 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.dbias) {
-    if ((e = launch_bias_tiles(p, a.bias, bias_k, 1, s)) != hipSuccess) return e;
     float* target = groups == 1 ? a.dbias : dbias_part;
     if ((e = launch_dbias_pipe(p, a, bias_k, groups, target, s)) != hipSuccess) return e;
     if (groups > 1) {

@@ -74,6 +74,9 @@ size_t bwd_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_fwd_mfma(const Problem& p, const FwdArgs& a, void* ws, hipStream_t s);
 hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& a, void* ws, hipStream_t s);
 
+// dQ (kernels_bwd_dq.hip); bias_q is the query-lane tiled bias.
+hipError_t launch_dq_pipe(const Problem& p, const BwdArgs& a, const float* bias_q, hipStream_t s);
+
 // dK, dV (kernels_bwd_dkdv.hip); bias_k is the key-lane tiled bias.
 hipError_t launch_dkdv_pipe(const Problem& p, const BwdArgs& a, const float* bias_k, hipStream_t s);
 

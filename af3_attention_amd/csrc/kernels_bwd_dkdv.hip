@@ -12,7 +12,8 @@
 // operands are staged in LDS with direct copies, double buffered.  Tiles are
 // S = Q K^T (queries x keys), so each lane holds one key:
 //   S  = Q K^T + sqrt(d) bias + sqrt(d) (mask - lse)   (bias: accumulator input,
-//        loaded one block ahead; mask and lse: one extra MFMA step)
+//        loaded a block ahead into alternating registers; mask and lse: one
+//        extra MFMA step)
 //   dP = dO V^T - D                                   (D: one extra MFMA step)
 //   P = exp2(S log2(e)/sqrt(d)),  dS = P dP
 // and P, dS in registers, packed to bf16, are directly the B operands of
@@ -111,13 +112,23 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
     b[0] = load_bias_tile(bias_k + bias_tile_offset(h, 2 * qb, kt, nt), lane);
     b[1] = load_bias_tile(bias_k + bias_tile_offset(h, 2 * qb + 1, kt, nt), lane);
   };
-  f32x16 bias[2];
+  f32x16 bias_reg[2][2];  // block qb uses set qb % 2
 
   auto step = [&](int qb, auto stage_c) {
     constexpr int s = decltype(stage_c)::value;
-    // Block qb was issued during the previous block, before that block's bias loads (8).
-    wait_vmcnt<8>();
+    // Block qb's copies were the last memory operations issued (at the start of
+    // the previous block, after its bias loads).
+    wait_vmcnt<0>();
     barrier();
+    // Start block qb + 1 at once: its bias into the other register set, then its
+    // copies into the other buffer (read during the previous block).  Issued in
+    // this order, the compiler's wait for this block's bias (below) leaves the
+    // copies in flight.
+    if (qb + 1 < nqb) {
+      load_bias(bias_reg[s ^ 1], qb + 1);
+      issue_block(qb + 1, std::integral_constant<int, s ^ 1>());
+    }
+    f32x16 (&bias)[2] = bias_reg[s];
     const uint32_t st = lds0 + s * STAGE;
     const uint32_t tq = st + (2 * wr) * TB, tdo = st + (2 * wr + 1) * TB;
     const uint32_t qaug_lds = st + NT * TB + wr * kBlk * 16;
@@ -137,14 +148,6 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
 #pragma unroll
       for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tdo, t * 32, ks, lane), vop[ks], dp);
       dp = mma(dp_q, dp_key, dp);
-
-      // Once the first tile's logits are issued, start the next block: its copies
-      // into the other buffer (read two blocks ago), then its bias (into the
-      // registers this tile just consumed).
-      if (t == 1 && qb + 1 < nqb) {
-        issue_block(qb + 1, std::integral_constant<int, s ^ 1>());
-        load_bias(bias, qb + 1);
-      }
 
       u32x4 pb[2], dsb[2];
 #pragma unroll
@@ -170,8 +173,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
     }
   };
 
+  load_bias(bias_reg[0], 0);
   issue_block(0, std::integral_constant<int, 0>());
-  load_bias(bias, 0);
   for (int qb = 0; qb < nqb; qb += 2) {
     step(qb, std::integral_constant<int, 0>());
     if (qb + 1 < nqb) step(qb + 1, std::integral_constant<int, 1>());

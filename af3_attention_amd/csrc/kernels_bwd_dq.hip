@@ -1,0 +1,190 @@
+// dQ of pair-biased 3D attention (bf16 MFMA, gfx950).
+//
+// The backward recomputes the probabilities from the saved logsumexp (MegaFold
+// pages, gist.science technical summary, Methodik section 1 "EvoFlash-3D": the
+// memory-efficient kernel runs in the forward and the backward).  With
+// dS = P * (dP - D):  dQ[j] = sum_k dS[j,k] K[k] / sqrt(d).
+//
+// Workgroup = 4 waves = 64 queries of two rows (r, r+1) of one head; wave w owns
+// the 32 queries 32 (w & 1).. of row r + (w >> 1) and keeps their dQ in
+// registers while it walks all keys in blocks of 64.  K, V and the rows'
+// per-key split operands are staged in LDS with direct copies, double buffered.
+// Tiles are S^T = K Q^T (keys x queries), so each lane holds one query:
+//   S^T  = K Q^T + sqrt(d) bias^T + sqrt(d) (mask - lse)  (bias: accumulator
+//          input, loaded a block ahead; mask and lse: one extra MFMA step)
+//   dP^T = V dO^T - D                                    (D: one extra MFMA step)
+//   P = exp2(S log2(e)/sqrt(d)),  dS = P dP
+// and dS^T in registers, packed to bf16, is directly the B operand of
+// dQ^T += K^T dS^T, whose A operand comes from transposing LDS reads of K.
+
+#include <algorithm>
+#include <type_traits>
+
+#include "pipe_common.h"
+
+namespace evo {
+namespace {
+
+using namespace mfma;
+using namespace pipe;
+
+constexpr int kDqRows = 2;     // attention rows per workgroup
+constexpr int kDqQueries = 64; // queries per workgroup (32 per wave)
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_q,
+                                                         int nt) {
+  constexpr int TB = Tile<D>::BYTES;                    // 64 keys
+  constexpr int NT = 2 * kDqRows;                       // K, V of each row
+  constexpr int STAGE = NT * TB + kDqRows * kBlk * 16;  // + key-side operands
+  constexpr int KS = Shape<D>::KS, DB = Shape<D>::DB;
+  using St = Stager<D, NT>;
+  __shared__ __align__(16) char lds[2 * STAGE + 1024];
+  constexpr int DUMMY = 2 * STAGE;
+
+  const int nqb = (p.N + kDqQueries - 1) / kDqQueries;
+  const int nrp = (p.R + kDqRows - 1) / kDqRows;
+  int blk = xcd_logical_block(blockIdx.x, nqb * nrp * p.H);
+  const int qb = blk % nqb;
+  blk /= nqb;
+  const int rp = blk % nrp;
+  const int h = blk / nrp;
+  const int wave = wave_id(), lane = threadIdx.x & 63, half = lane >> 5;
+  const int wr = wave >> 1, wq = wave & 1;  // row, query tile of this wave
+  const bool row_valid = kDqRows * rp + wr < p.R;
+  const int r = row_valid ? kDqRows * rp + wr : kDqRows * rp;  // an invalid row aliases a valid one
+  const int j = qb * kDqQueries + wq * 32 + (lane & 31);       // this lane's query
+  const int nkb = (p.N + kBlk - 1) / kBlk;
+
+  const float sd = sqrtf(static_cast<float>(D));
+  const float c1 = kLog2e / sd;
+  const uint32_t lds0 = lds_addr(lds);
+  St stager;
+  stager.init(wave, lane, static_cast<uint32_t>(p.pos_stride * p.H * D * 2));
+  TileReads<D> rd;
+  rd.init(lane);
+
+  // Per-wave constants: Q and dO of this lane's query (B operands), the
+  // query-side split operands, the dQ^T accumulator.
+  u32x4 qop[KS], doop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qop[ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.q), r, j, h, ks, half);
+    doop[ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.dout), r, j, h, ks, half);
+  }
+  const u32x4 qa =
+      static_cast<const u32x4*>(a.qaug)[(static_cast<int64_t>(r) * p.H + h) * p.N + min(j, p.N - 1)];
+  const u32x4 s_q = {qa[0], qa[1], kBf16One | (kBf16One << 16), 0u};
+  const u32x4 dp_q = {qa[2], qa[3], 0u, 0u};
+  const u32x4 dp_key = key_aug_unit(lane);
+  f32x16 dq_acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq_acc[db][e] = 0.f;
+
+  // Staged per block: K r0, V r0, K r1, V r1, then the key-side operands of both
+  // rows (64 entries of 16 bytes each).
+  const char* base[NT];
+  const u32x4* kaug_row[kDqRows];
+#pragma unroll
+  for (int i = 0; i < kDqRows; ++i) {
+    const int ri = min(kDqRows * rp + i, p.R - 1);
+    const int64_t rh = row_head_offset(p, ri, h);
+    base[2 * i] = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + rh));
+    base[2 * i + 1] = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + rh));
+    kaug_row[i] = uniform_ptr(static_cast<const u32x4*>(a.kaug) + static_cast<int64_t>(ri) * p.N);
+  }
+  auto issue_block = [&](int kb, auto stage_c) {
+    constexpr int s = decltype(stage_c)::value;
+    const uint32_t st = lds0 + s * STAGE;
+    stager.issue(st, base, kb * kBlk, p.N, wave, lds0 + DUMMY);
+    if (wave < kDqRows)
+      copy_rows16(wave == 0 ? kaug_row[0] : kaug_row[1], kb * kBlk, p.N, st + NT * TB + wave * kBlk * 16, lane);
+    else
+      copy16_to_lds(uniform_ptr(kaug_row[0]), 0u, lds0 + DUMMY);
+  };
+
+  // sqrt(d) * bias^T of the wave's queries for the two 32-key tiles of a block.
+  const int qt = qb * (kDqQueries / 32) + wq;
+  auto load_bias = [&](f32x16 (&b)[2], int kb) {
+    b[0] = load_bias_tile(bias_q + bias_tile_offset(h, qt, 2 * kb, nt), lane);
+    b[1] = load_bias_tile(bias_q + bias_tile_offset(h, qt, 2 * kb + 1, nt), lane);
+  };
+  f32x16 bias_reg[2][2];  // block kb uses set kb % 2
+
+  auto step = [&](int kb, auto stage_c) {
+    constexpr int s = decltype(stage_c)::value;
+    // Block kb's copies were the last memory operations issued (at the start of
+    // the previous block, after its bias loads).
+    wait_vmcnt<0>();
+    barrier();
+    // Start block kb + 1 at once: its bias into the other register set, then its
+    // copies into the other buffer (read during the previous block).
+    if (kb + 1 < nkb) {
+      load_bias(bias_reg[s ^ 1], kb + 1);
+      issue_block(kb + 1, std::integral_constant<int, s ^ 1>());
+    }
+    f32x16 (&bias)[2] = bias_reg[s];
+    const uint32_t st = lds0 + s * STAGE;
+    const uint32_t tk = st + (2 * wr) * TB, tv = st + (2 * wr + 1) * TB;
+    const uint32_t kaug_lds = st + NT * TB + wr * kBlk * 16;
+
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      u32x4 s_key = lds_load16(kaug_lds + (mb * 32 + (lane & 31)) * 16);
+      if (half) s_key = u32x4{0u, 0u, 0u, 0u};
+      f32x16 sacc = mma(rd.rows_operand(tk, mb * 32, 0, lane), qop[0], bias[mb]);
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tk, mb * 32, ks, lane), qop[ks], sacc);
+      sacc = mma(s_key, s_q, sacc);
+      f32x16 dp = mma(rd.rows_operand(tv, mb * 32, 0, lane), doop[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tv, mb * 32, ks, lane), doop[ks], dp);
+      dp = mma(dp_key, dp_q, dp);
+
+      u32x4 dsb[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsv[e] = fast_exp2(sacc[8 * u + e] * c1) * dp[8 * u + e];
+        dsb[u] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                       pack_bf16(dsv[6], dsv[7])};
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dq_acc[db] = mma(rd.tr_operand(tk, db, mb * 32, u), dsb[u], dq_acc[db]);
+    }
+  };
+
+  load_bias(bias_reg[0], 0);
+  issue_block(0, std::integral_constant<int, 0>());
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(kb, std::integral_constant<int, 0>());
+    if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>());
+  }
+
+  if (!row_valid || j >= p.N) return;
+  store_dT<D>(static_cast<uint16_t*>(a.dq) + elem_offset(p, r, j, h), dq_acc, 1.f / sd, half);
+}
+
+}  // namespace
+
+hipError_t launch_dq_pipe(const Problem& p, const BwdArgs& a, const float* bias_q, hipStream_t s) {
+  const int64_t blocks =
+      static_cast<int64_t>((p.N + kDqQueries - 1) / kDqQueries) * p.H * ((p.R + kDqRows - 1) / kDqRows);
+  const int nt = bias_tiles(p.N);
+  KernelTimer timer("bwd_dq_mfma", s);
+  switch (p.D) {
+    case 8: hipLaunchKernelGGL((dq_pipe_kernel<8>), dim3(blocks), dim3(256), 0, s, p, a, bias_q, nt); break;
+    case 16: hipLaunchKernelGGL((dq_pipe_kernel<16>), dim3(blocks), dim3(256), 0, s, p, a, bias_q, nt); break;
+    case 32: hipLaunchKernelGGL((dq_pipe_kernel<32>), dim3(blocks), dim3(256), 0, s, p, a, bias_q, nt); break;
+    case 64: hipLaunchKernelGGL((dq_pipe_kernel<64>), dim3(blocks), dim3(256), 0, s, p, a, bias_q, nt); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace evo

@@ -5,11 +5,12 @@
 // memory-efficient kernel runs in the forward and the backward).  With
 // dS = P * (dP - D):  dQ[j] = sum_k dS[j,k] K[k] / sqrt(d).
 //
-// Workgroup = 4 waves = 64 queries of two rows (r, r+1) of one head; wave w owns
-// the 32 queries 32 (w & 1).. of row r + (w >> 1) and keeps their dQ in
-// registers while it walks all keys in blocks of 64.  K, V and the rows'
-// per-key split operands are staged in LDS with direct copies, double buffered.
-// Tiles are S^T = K Q^T (keys x queries), so each lane holds one query:
+// Workgroup = 4 waves = 128 queries of two rows (r, r+1) of one head (one row at
+// d = 64); wave w owns the 32 queries 32 w.. of both rows, so each bias tile it
+// loads serves two rows, and keeps their dQ in registers while it walks all keys
+// in blocks of 64.  K, V and the rows' per-key split operands are staged in LDS
+// with direct copies, double buffered, and shared by the four waves.  Tiles are S^T = K Q^T (keys x
+// queries), so each lane holds one query:
 //   S^T  = K Q^T + sqrt(d) bias^T + sqrt(d) (mask - lse)  (bias: accumulator
 //          input, loaded a block ahead; mask and lse: one extra MFMA step)
 //   dP^T = V dO^T - D                                    (D: one extra MFMA step)
@@ -28,12 +29,16 @@ namespace {
 using namespace mfma;
 using namespace pipe;
 
-constexpr int kDqRows = 2;     // attention rows per workgroup
-constexpr int kDqQueries = 64; // queries per workgroup (32 per wave)
+constexpr int kDqQueries = 128;  // queries per workgroup (32 per wave)
+// Attention rows per workgroup (and per wave): two, or one at d = 64 where two
+// rows' operands and accumulators would not fit the registers.
+template <int D>
+constexpr int dq_rows() { return D >= 64 ? 1 : 2; }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_q,
                                                          int nt) {
+  constexpr int kDqRows = dq_rows<D>();
   constexpr int TB = Tile<D>::BYTES;                    // 64 keys
   constexpr int NT = 2 * kDqRows;                       // K, V of each row
   constexpr int STAGE = NT * TB + kDqRows * kBlk * 16;  // + key-side operands
@@ -50,10 +55,9 @@ __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, c
   const int rp = blk % nrp;
   const int h = blk / nrp;
   const int wave = wave_id(), lane = threadIdx.x & 63, half = lane >> 5;
-  const int wr = wave >> 1, wq = wave & 1;  // row, query tile of this wave
-  const bool row_valid = kDqRows * rp + wr < p.R;
-  const int r = row_valid ? kDqRows * rp + wr : kDqRows * rp;  // an invalid row aliases a valid one
-  const int j = qb * kDqQueries + wq * 32 + (lane & 31);       // this lane's query
+  const int j0 = qb * kDqQueries + wave * 32;
+  const int j = j0 + (lane & 31);  // this lane's query
+  const bool wave_active = j0 < p.N;
   const int nkb = (p.N + kBlk - 1) / kBlk;
 
   const float sd = sqrtf(static_cast<float>(D));
@@ -64,49 +68,53 @@ __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, c
   TileReads<D> rd;
   rd.init(lane);
 
-  // Per-wave constants: Q and dO of this lane's query (B operands), the
-  // query-side split operands, the dQ^T accumulator.
-  u32x4 qop[KS], doop[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qop[ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.q), r, j, h, ks, half);
-    doop[ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.dout), r, j, h, ks, half);
-  }
-  const u32x4 qa =
-      static_cast<const u32x4*>(a.qaug)[(static_cast<int64_t>(r) * p.H + h) * p.N + min(j, p.N - 1)];
-  const u32x4 s_q = {qa[0], qa[1], kBf16One | (kBf16One << 16), 0u};
-  const u32x4 dp_q = {qa[2], qa[3], 0u, 0u};
-  const u32x4 dp_key = key_aug_unit(lane);
-  f32x16 dq_acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dq_acc[db][e] = 0.f;
-
-  // Staged per block: K r0, V r0, K r1, V r1, then the key-side operands of both
-  // rows (64 entries of 16 bytes each).
+  // Per row: Q and dO of this lane's query (B operands), the query-side split
+  // operands, the dQ^T accumulator.
+  bool rvalid[kDqRows];
+  int rr[kDqRows];
+  u32x4 qop[kDqRows][KS], doop[kDqRows][KS], s_q[kDqRows], dp_q[kDqRows];
+  f32x16 dq_acc[kDqRows][DB];
   const char* base[NT];
   const u32x4* kaug_row[kDqRows];
 #pragma unroll
   for (int i = 0; i < kDqRows; ++i) {
-    const int ri = min(kDqRows * rp + i, p.R - 1);
-    const int64_t rh = row_head_offset(p, ri, h);
+    rvalid[i] = kDqRows * rp + i < p.R;
+    rr[i] = rvalid[i] ? kDqRows * rp + i : kDqRows * rp;  // an invalid row aliases a valid one
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qop[i][ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.q), rr[i], j, h, ks, half);
+      doop[i][ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.dout), rr[i], j, h, ks, half);
+    }
+    const u32x4 qa =
+        static_cast<const u32x4*>(a.qaug)[(static_cast<int64_t>(rr[i]) * p.H + h) * p.N + min(j, p.N - 1)];
+    s_q[i] = u32x4{qa[0], qa[1], kBf16One | (kBf16One << 16), 0u};
+    dp_q[i] = u32x4{qa[2], qa[3], 0u, 0u};
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dq_acc[i][db][e] = 0.f;
+    // Staged per block: K r0, V r0, K r1, V r1, then the key-side operands of both
+    // rows (64 entries of 16 bytes each).
+    const int64_t rh = row_head_offset(p, rr[i], h);
     base[2 * i] = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + rh));
     base[2 * i + 1] = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + rh));
-    kaug_row[i] = uniform_ptr(static_cast<const u32x4*>(a.kaug) + static_cast<int64_t>(ri) * p.N);
+    kaug_row[i] = uniform_ptr(static_cast<const u32x4*>(a.kaug) + static_cast<int64_t>(rr[i]) * p.N);
   }
+  const u32x4 dp_key = key_aug_unit(lane);
+
   auto issue_block = [&](int kb, auto stage_c) {
     constexpr int s = decltype(stage_c)::value;
     const uint32_t st = lds0 + s * STAGE;
     stager.issue(st, base, kb * kBlk, p.N, wave, lds0 + DUMMY);
     if (wave < kDqRows)
-      copy_rows16(wave == 0 ? kaug_row[0] : kaug_row[1], kb * kBlk, p.N, st + NT * TB + wave * kBlk * 16, lane);
+      copy_rows16(wave == 0 ? kaug_row[0] : kaug_row[kDqRows - 1], kb * kBlk, p.N, st + NT * TB + wave * kBlk * 16,
+                  lane);
     else
       copy16_to_lds(uniform_ptr(kaug_row[0]), 0u, lds0 + DUMMY);
   };
 
   // sqrt(d) * bias^T of the wave's queries for the two 32-key tiles of a block.
-  const int qt = qb * (kDqQueries / 32) + wq;
+  const int qt = min(qb * (kDqQueries / 32) + wave, nt - 1);
   auto load_bias = [&](f32x16 (&b)[2], int kb) {
     b[0] = load_bias_tile(bias_q + bias_tile_offset(h, qt, 2 * kb, nt), lane);
     b[1] = load_bias_tile(bias_q + bias_tile_offset(h, qt, 2 * kb + 1, nt), lane);
@@ -125,37 +133,42 @@ __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, c
       load_bias(bias_reg[s ^ 1], kb + 1);
       issue_block(kb + 1, std::integral_constant<int, s ^ 1>());
     }
+    if (!wave_active) return;
     f32x16 (&bias)[2] = bias_reg[s];
     const uint32_t st = lds0 + s * STAGE;
-    const uint32_t tk = st + (2 * wr) * TB, tv = st + (2 * wr + 1) * TB;
-    const uint32_t kaug_lds = st + NT * TB + wr * kBlk * 16;
 
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      u32x4 s_key = lds_load16(kaug_lds + (mb * 32 + (lane & 31)) * 16);
-      if (half) s_key = u32x4{0u, 0u, 0u, 0u};
-      f32x16 sacc = mma(rd.rows_operand(tk, mb * 32, 0, lane), qop[0], bias[mb]);
+    for (int i = 0; i < kDqRows; ++i) {
+      const uint32_t tk = st + (2 * i) * TB, tv = st + (2 * i + 1) * TB;
+      const uint32_t kaug_lds = st + NT * TB + i * kBlk * 16;
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tk, mb * 32, ks, lane), qop[ks], sacc);
-      sacc = mma(s_key, s_q, sacc);
-      f32x16 dp = mma(rd.rows_operand(tv, mb * 32, 0, lane), doop[0], f32x16{});
+      for (int mb = 0; mb < 2; ++mb) {
+        u32x4 s_key = lds_load16(kaug_lds + (mb * 32 + (lane & 31)) * 16);
+        if (half) s_key = u32x4{0u, 0u, 0u, 0u};
+        f32x16 sacc = mma(rd.rows_operand(tk, mb * 32, 0, lane), qop[i][0], bias[mb]);
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tv, mb * 32, ks, lane), doop[ks], dp);
-      dp = mma(dp_key, dp_q, dp);
+        for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tk, mb * 32, ks, lane), qop[i][ks], sacc);
+        sacc = mma(s_key, s_q[i], sacc);
+        f32x16 dp = mma(rd.rows_operand(tv, mb * 32, 0, lane), doop[i][0], f32x16{});
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tv, mb * 32, ks, lane), doop[i][ks], dp);
+        dp = mma(dp_key, dp_q[i], dp);
 
-      u32x4 dsb[2];
+        u32x4 dsb[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float dsv[8];
+        for (int u = 0; u < 2; ++u) {
+          float dsv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dsv[e] = fast_exp2(sacc[8 * u + e] * c1) * dp[8 * u + e];
-        dsb[u] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
-                       pack_bf16(dsv[6], dsv[7])};
+          for (int e = 0; e < 8; ++e) dsv[e] = fast_exp2(sacc[8 * u + e] * c1) * dp[8 * u + e];
+          dsb[u] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                         pack_bf16(dsv[6], dsv[7])};
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            dq_acc[i][db] = mma(rd.tr_operand(tk, db, mb * 32, u), dsb[u], dq_acc[i][db]);
       }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) dq_acc[db] = mma(rd.tr_operand(tk, db, mb * 32, u), dsb[u], dq_acc[db]);
     }
   };
 
@@ -166,15 +179,18 @@ __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, c
     if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>());
   }
 
-  if (!row_valid || j >= p.N) return;
-  store_dT<D>(static_cast<uint16_t*>(a.dq) + elem_offset(p, r, j, h), dq_acc, 1.f / sd, half);
+  if (!wave_active || j >= p.N) return;
+#pragma unroll
+  for (int i = 0; i < kDqRows; ++i)
+    if (rvalid[i])
+      store_dT<D>(static_cast<uint16_t*>(a.dq) + elem_offset(p, rr[i], j, h), dq_acc[i], 1.f / sd, half);
 }
 
 }  // namespace
 
 hipError_t launch_dq_pipe(const Problem& p, const BwdArgs& a, const float* bias_q, hipStream_t s) {
-  const int64_t blocks =
-      static_cast<int64_t>((p.N + kDqQueries - 1) / kDqQueries) * p.H * ((p.R + kDqRows - 1) / kDqRows);
+  const int rows = p.D >= 64 ? dq_rows<64>() : dq_rows<32>();
+  const int64_t blocks = static_cast<int64_t>((p.N + kDqQueries - 1) / kDqQueries) * p.H * ((p.R + rows - 1) / rows);
   const int nt = bias_tiles(p.N);
   KernelTimer timer("bwd_dq_mfma", s);
   switch (p.D) {

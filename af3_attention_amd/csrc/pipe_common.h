@@ -198,20 +198,22 @@ struct Stager {
   static constexpr int NIT = (TOTAL + THREADS - 1) / THREADS;  // copies per thread per stage
   static_assert(TOTAL % 64 == 0, "stage must be a multiple of 64 chunks");
   uint32_t voff[NIT];  // byte offset of the chunk from position x0 of its slab
-  int xr[NIT];         // position of the chunk within the block
-  int cb[NIT];         // byte offset of the chunk within its position
   uint32_t pstride;    // bytes between consecutive positions
 
+  // Position and byte offset within the position of the chunk that copy `it` of
+  // this lane writes.
+  __device__ __forceinline__ static void chunk_of(int it, int wave, int lane, int& x, int& cbyte) {
+    const int within = (it * THREADS + wave * 64 + lane) % PER_TILE;
+    x = within / CH;
+    cbyte = ((within % CH) ^ Tile<D>::swz(x)) * 16;
+  }
   __device__ __forceinline__ void init(int wave, int lane, uint32_t pstride_bytes) {
     pstride = pstride_bytes;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int within = (it * THREADS + wave * 64 + lane) % PER_TILE;
-      const int x = within / CH;
-      const int p = (within % CH) ^ Tile<D>::swz(x);
-      xr[it] = x;
-      cb[it] = p * 16;
-      voff[it] = static_cast<uint32_t>(x) * pstride_bytes + p * 16;
+      int x, cbyte;
+      chunk_of(it, wave, lane, x, cbyte);
+      voff[it] = static_cast<uint32_t>(x) * pstride_bytes + cbyte;
     }
   }
   // Tile index of copy `it` of `wave` (uniform; a compile-time constant when a
@@ -237,8 +239,10 @@ struct Stager {
     if (full) {
       copy16_to_lds(uniform_ptr(b + static_cast<size_t>(x0) * pstride), voff[IT], dst);
     } else {
-      const int pos = min(x0 + xr[IT], n - 1);
-      copy16_to_lds(b + static_cast<size_t>(pos) * pstride + cb[IT], dst);
+      int x, cbyte;
+      chunk_of(IT, wave, static_cast<int>(threadIdx.x & 63), x, cbyte);
+      const int pos = min(x0 + x, n - 1);
+      copy16_to_lds(b + static_cast<size_t>(pos) * pstride + cbyte, dst);
     }
   }
   template <int IT = 0>

@@ -6,11 +6,12 @@
 // "EvoFlash-3D").  With dS = P * (dP - D):
 //   dV[k] = sum_j P[j,k] dO[j],   dK[k] = sum_j dS[j,k] Q[j] / sqrt(d).
 //
-// Workgroup = 4 waves = 64 keys of two rows (r, r+1) of one head; wave w owns the
-// 32 keys 32 (w & 1).. of row r + (w >> 1) and keeps their dK, dV in registers
-// while it walks all queries in blocks of 64.  Q, dO and the rows' per-query split
-// operands are staged in LDS with direct copies, double buffered.  Tiles are
-// S = Q K^T (queries x keys), so each lane holds one key:
+// Workgroup = 4 waves = 128 keys of two rows (r, r+1) of one head (one row at
+// d = 64); wave w owns the 32 keys 32 w.. of both rows, so each bias tile it
+// loads serves two rows, and keeps their dK, dV in registers while it walks all
+// queries in blocks of 64.  Q, dO and the rows' per-query split operands are
+// staged in LDS with direct copies, double buffered, and shared by the four
+// waves.  Tiles are S = Q K^T (queries x keys), so each lane holds one key:
 //   S  = Q K^T + sqrt(d) bias + sqrt(d) (mask - lse)   (bias: accumulator input,
 //        loaded a block ahead into alternating registers; mask and lse: one
 //        extra MFMA step)
@@ -31,32 +32,35 @@ namespace {
 using namespace mfma;
 using namespace pipe;
 
-constexpr int kKvRows = 2;   // attention rows per workgroup
-constexpr int kKvKeys = 64;  // keys per workgroup (32 per wave)
+constexpr int kKvKeys = 128;  // keys per workgroup (32 per wave)
+// Attention rows per workgroup (and per wave): two, or one at d = 64 where two
+// rows' operands and accumulators would not fit the registers.
+template <int D>
+constexpr int kv_rows() { return D >= 64 ? 1 : 2; }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_k,
                                                            int nt) {
-  constexpr int TB = Tile<D>::BYTES;                     // 64 queries
-  constexpr int NT = 2 * kKvRows;                        // Q, dO of each row
-  constexpr int STAGE = NT * TB + kKvRows * kBlk * 16;   // + query-side operands
+  constexpr int RW = kv_rows<D>();
+  constexpr int TB = Tile<D>::BYTES;               // 64 queries
+  constexpr int NT = 2 * RW;                       // Q, dO of each row
+  constexpr int STAGE = NT * TB + RW * kBlk * 16;  // + query-side operands
   constexpr int KS = Shape<D>::KS, DB = Shape<D>::DB;
   using St = Stager<D, NT>;
   __shared__ __align__(16) char lds[2 * STAGE + 1024];
   constexpr int DUMMY = 2 * STAGE;
 
   const int nkb = (p.N + kKvKeys - 1) / kKvKeys;
-  const int nrp = (p.R + kKvRows - 1) / kKvRows;
+  const int nrp = (p.R + RW - 1) / RW;
   int blk = xcd_logical_block(blockIdx.x, nkb * nrp * p.H);
   const int kb = blk % nkb;
   blk /= nkb;
   const int rp = blk % nrp;
   const int h = blk / nrp;
   const int wave = wave_id(), lane = threadIdx.x & 63, half = lane >> 5;
-  const int wr = wave >> 1, wk = wave & 1;  // row, key tile of this wave
-  const bool row_valid = kKvRows * rp + wr < p.R;
-  const int r = row_valid ? kKvRows * rp + wr : kKvRows * rp;  // an invalid row aliases a valid one
-  const int key = kb * kKvKeys + wk * 32 + (lane & 31);         // this lane's key
+  const int k0w = kb * kKvKeys + wave * 32;  // first key of this wave
+  const int key = k0w + (lane & 31);         // this lane's key
+  const bool wave_active = k0w < p.N;
   const int nqb = (p.N + kBlk - 1) / kBlk;
 
   const float sd = sqrtf(static_cast<float>(D));
@@ -67,47 +71,50 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
   TileReads<D> rd;
   rd.init(lane);
 
-  // Per-wave constants: K and V of this lane's key (B operands), the key-side
-  // split operands, dK^T and dV^T accumulators.
-  u32x4 kop[KS], vop[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kop[ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.k), r, key, h, ks, half);
-    vop[ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.v), r, key, h, ks, half);
-  }
-  u32x4 s_key = static_cast<const u32x4*>(a.kaug)[static_cast<int64_t>(r) * p.N + min(key, p.N - 1)];
-  if (half) s_key = u32x4{0u, 0u, 0u, 0u};
-  const u32x4 dp_key = key_aug_unit(lane);
-  f32x16 dk_acc[DB], dv_acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dk_acc[db][e] = dv_acc[db][e] = 0.f;
-
-  // Staged per block: Q r0, dO r0, Q r1, dO r1, then the query-side operands of
-  // both rows (64 entries of 16 bytes each).
+  // Per row: K and V of this lane's key (B operands), the key-side split
+  // operands, dK^T and dV^T accumulators.
+  bool rvalid[RW];
+  int rr[RW];
+  u32x4 kop[RW][KS], vop[RW][KS], s_key[RW];
+  f32x16 dk_acc[RW][DB], dv_acc[RW][DB];
   const char* base[NT];
-  const u32x4* qaug_row[kKvRows];
+  const u32x4* qaug_row[RW];
 #pragma unroll
-  for (int i = 0; i < kKvRows; ++i) {
-    const int ri = min(kKvRows * rp + i, p.R - 1);
-    const int64_t rh = row_head_offset(p, ri, h);
+  for (int i = 0; i < RW; ++i) {
+    rvalid[i] = RW * rp + i < p.R;
+    rr[i] = rvalid[i] ? RW * rp + i : RW * rp;  // an invalid row aliases a valid one
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kop[i][ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.k), rr[i], key, h, ks, half);
+      vop[i][ks] = global_operand<D>(p, static_cast<const uint16_t*>(a.v), rr[i], key, h, ks, half);
+    }
+    s_key[i] = static_cast<const u32x4*>(a.kaug)[static_cast<int64_t>(rr[i]) * p.N + min(key, p.N - 1)];
+    if (half) s_key[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dk_acc[i][db][e] = dv_acc[i][db][e] = 0.f;
+    // Staged per block: Q r0, dO r0, Q r1, dO r1, then the query-side operands of
+    // both rows (64 entries of 16 bytes each).
+    const int64_t rh = row_head_offset(p, rr[i], h);
     base[2 * i] = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.q) + rh));
     base[2 * i + 1] = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.dout) + rh));
-    qaug_row[i] = uniform_ptr(static_cast<const u32x4*>(a.qaug) + (static_cast<int64_t>(ri) * p.H + h) * p.N);
+    qaug_row[i] = uniform_ptr(static_cast<const u32x4*>(a.qaug) + (static_cast<int64_t>(rr[i]) * p.H + h) * p.N);
   }
+  const u32x4 dp_key = key_aug_unit(lane);
+
   auto issue_block = [&](int qb, auto stage_c) {
     constexpr int s = decltype(stage_c)::value;
     const uint32_t st = lds0 + s * STAGE;
     stager.issue(st, base, qb * kBlk, p.N, wave, lds0 + DUMMY);
-    if (wave < kKvRows)
-      copy_rows16(wave == 0 ? qaug_row[0] : qaug_row[1], qb * kBlk, p.N, st + NT * TB + wave * kBlk * 16, lane);
+    if (wave < RW)
+      copy_rows16(wave == 0 ? qaug_row[0] : qaug_row[RW - 1], qb * kBlk, p.N, st + NT * TB + wave * kBlk * 16, lane);
     else
       copy16_to_lds(uniform_ptr(qaug_row[0]), 0u, lds0 + DUMMY);
   };
 
   // sqrt(d) * bias of the wave's keys for the two 32-query tiles of a block.
-  const int kt = kb * (kKvKeys / 32) + wk;
+  const int kt = min(kb * (kKvKeys / 32) + wave, nt - 1);
   auto load_bias = [&](f32x16 (&b)[2], int qb) {
     b[0] = load_bias_tile(bias_k + bias_tile_offset(h, 2 * qb, kt, nt), lane);
     b[1] = load_bias_tile(bias_k + bias_tile_offset(h, 2 * qb + 1, kt, nt), lane);
@@ -128,48 +135,52 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
       load_bias(bias_reg[s ^ 1], qb + 1);
       issue_block(qb + 1, std::integral_constant<int, s ^ 1>());
     }
+    if (!wave_active) return;
     f32x16 (&bias)[2] = bias_reg[s];
     const uint32_t st = lds0 + s * STAGE;
-    const uint32_t tq = st + (2 * wr) * TB, tdo = st + (2 * wr + 1) * TB;
-    const uint32_t qaug_lds = st + NT * TB + wr * kBlk * 16;
 
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int jl = t * 32 + (lane & 31);
-      const u32x4 qa = lds_load16(qaug_lds + jl * 16);
-      const u32x4 s_q = qb * kBlk + jl < p.N ? u32x4{qa[0], qa[1], kBf16One | (kBf16One << 16), 0u}
-                                             : dead_query_aug();
-      const u32x4 dp_q = {qa[2], qa[3], 0u, 0u};
-      f32x16 sacc = mma(rd.rows_operand(tq, t * 32, 0, lane), kop[0], bias[t]);
+    for (int i = 0; i < RW; ++i) {
+      const uint32_t tq = st + (2 * i) * TB, tdo = st + (2 * i + 1) * TB;
+      const uint32_t qaug_lds = st + NT * TB + i * kBlk * 16;
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tq, t * 32, ks, lane), kop[ks], sacc);
-      sacc = mma(s_q, s_key, sacc);
-      f32x16 dp = mma(rd.rows_operand(tdo, t * 32, 0, lane), vop[0], f32x16{});
+      for (int t = 0; t < 2; ++t) {
+        const int jl = t * 32 + (lane & 31);
+        const u32x4 qa = lds_load16(qaug_lds + jl * 16);
+        const u32x4 s_q = qb * kBlk + jl < p.N ? u32x4{qa[0], qa[1], kBf16One | (kBf16One << 16), 0u}
+                                               : dead_query_aug();
+        const u32x4 dp_q = {qa[2], qa[3], 0u, 0u};
+        f32x16 sacc = mma(rd.rows_operand(tq, t * 32, 0, lane), kop[i][0], bias[t]);
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tdo, t * 32, ks, lane), vop[ks], dp);
-      dp = mma(dp_q, dp_key, dp);
+        for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tq, t * 32, ks, lane), kop[i][ks], sacc);
+        sacc = mma(s_q, s_key[i], sacc);
+        f32x16 dp = mma(rd.rows_operand(tdo, t * 32, 0, lane), vop[i][0], f32x16{});
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tdo, t * 32, ks, lane), vop[i][ks], dp);
+        dp = mma(dp_q, dp_key, dp);
 
-      u32x4 pb[2], dsb[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float pv[8], dsv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(sacc[8 * u + e] * c1);
-          dsv[e] = pv[e] * dp[8 * u + e];
-        }
-        pb[u] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
-                      pack_bf16(pv[6], pv[7])};
-        dsb[u] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
-                       pack_bf16(dsv[6], dsv[7])};
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
+        u32x4 pb[2], dsb[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          dv_acc[db] = mma(rd.tr_operand(tdo, db, t * 32, u), pb[u], dv_acc[db]);
-          dk_acc[db] = mma(rd.tr_operand(tq, db, t * 32, u), dsb[u], dk_acc[db]);
+          float pv[8], dsv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = fast_exp2(sacc[8 * u + e] * c1);
+            dsv[e] = pv[e] * dp[8 * u + e];
+          }
+          pb[u] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                        pack_bf16(pv[6], pv[7])};
+          dsb[u] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                         pack_bf16(dsv[6], dsv[7])};
         }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            dv_acc[i][db] = mma(rd.tr_operand(tdo, db, t * 32, u), pb[u], dv_acc[i][db]);
+            dk_acc[i][db] = mma(rd.tr_operand(tq, db, t * 32, u), dsb[u], dk_acc[i][db]);
+          }
+      }
     }
   };
 
@@ -180,16 +191,21 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
     if (qb + 1 < nqb) step(qb + 1, std::integral_constant<int, 1>());
   }
 
-  if (!row_valid || key >= p.N) return;
-  const int64_t off = elem_offset(p, r, key, h);
-  store_dT<D>(static_cast<uint16_t*>(a.dv) + off, dv_acc, 1.f, half);
-  store_dT<D>(static_cast<uint16_t*>(a.dk) + off, dk_acc, 1.f / sd, half);
+  if (!wave_active || key >= p.N) return;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    if (!rvalid[i]) continue;
+    const int64_t off = elem_offset(p, rr[i], key, h);
+    store_dT<D>(static_cast<uint16_t*>(a.dv) + off, dv_acc[i], 1.f, half);
+    store_dT<D>(static_cast<uint16_t*>(a.dk) + off, dk_acc[i], 1.f / sd, half);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_dkdv_pipe(const Problem& p, const BwdArgs& a, const float* bias_k, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>((p.N + kKvKeys - 1) / kKvKeys) * p.H * ((p.R + kKvRows - 1) / kKvRows);
+  const int rows = p.D >= 64 ? kv_rows<64>() : kv_rows<32>();
+  const int64_t blocks = static_cast<int64_t>((p.N + kKvKeys - 1) / kKvKeys) * p.H * ((p.R + rows - 1) / rows);
   const int nt = bias_tiles(p.N);
   KernelTimer timer("bwd_dkdv_mfma", s);
   switch (p.D) {

@@ -8,25 +8,23 @@
 namespace evo {
 namespace {
 
-// Tiled layout (see pipe_common.h): one thread per output float.
+// Tiled layout (see pipe_common.h).  One workgroup per 32 x 32 block (query tile
+// qt, key tile kt) of one head: the block is read once (coalesced rows of 32 keys)
+// into LDS, then written in the query-lane order to out_q and, if out_k is not
+// NULL, in the key-lane order to out_k, each as 256 coalesced 16-byte stores.
 template <typename T>
-__global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __restrict__ bias, float* __restrict__ out,
-                                                         int nt, int orientation) {
-  const int64_t total = static_cast<int64_t>(p.H) * nt * nt * 1024;
+__global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __restrict__ bias, float* __restrict__ out_q,
+                                                         float* __restrict__ out_k, int nt) {
+  __shared__ float tile[32][33];  // [query][key], padded
+  const int kt = blockIdx.x % nt;
+  const int qt = (blockIdx.x / nt) % nt;
+  const int h = blockIdx.x / (nt * nt);
   const float sd = sqrtf(static_cast<float>(p.D));
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int e = static_cast<int>(idx & 3);
-    const int lane = static_cast<int>((idx >> 2) & 63);
-    const int g = static_cast<int>((idx >> 8) & 3);
-    const int64_t t = idx >> 10;
-    const int kt = static_cast<int>(t % nt);
-    const int qt = static_cast<int>((t / nt) % nt);
-    const int h = static_cast<int>(t / (static_cast<int64_t>(nt) * nt));
-    const int row = 8 * g + 4 * (lane >> 5) + e;  // accumulator row of register 4g+e
-    const int col = lane & 31;
-    const int j = qt * 32 + (orientation == 0 ? col : row);
-    const int k = kt * 32 + (orientation == 0 ? row : col);
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int jj = (t >> 5) + 8 * i, kk = t & 31;
+    const int j = qt * 32 + jj, k = kt * 32 + kk;
     float val;
     if (k >= p.N) {
       val = -INFINITY;
@@ -35,8 +33,20 @@ __global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __r
     } else {
       val = sd * Elem<T>::load(bias, (static_cast<int64_t>(h) * p.N + j) * p.N + k);
     }
-    out[idx] = val;
+    tile[jj][kk] = val;
   }
+  __syncthreads();
+  // Thread t writes floats 4t..4t+3 of the tile: register group g = t / 64 of lane
+  // l = t % 64, accumulator rows 8g + 4(l / 32) + e, column l % 32.
+  const int g = t >> 6, lane = t & 63;
+  const int row0 = 8 * g + 4 * (lane >> 5), col = lane & 31;
+  const int64_t off = (((static_cast<int64_t>(h) * nt + qt) * nt + kt) * 1024) + 4 * t;
+  // Query lanes: rows are keys, the column is the query.
+  *reinterpret_cast<float4*>(out_q + off) =
+      make_float4(tile[col][row0], tile[col][row0 + 1], tile[col][row0 + 2], tile[col][row0 + 3]);
+  if (out_k)  // key lanes: rows are queries, the column is the key
+    *reinterpret_cast<float4*>(out_k + off) =
+        make_float4(tile[row0][col], tile[row0 + 1][col], tile[row0 + 2][col], tile[row0 + 3][col]);
 }
 
 }  // namespace
@@ -46,13 +56,12 @@ size_t tiled_bias_bytes(const Problem& p) {
   return static_cast<size_t>(p.H) * nt * nt * 1024 * sizeof(float);
 }
 
-hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out, int orientation, hipStream_t s) {
+hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out_q, float* out_k, hipStream_t s) {
   const int nt = bias_tiles(p.N);
-  const int64_t total = static_cast<int64_t>(p.H) * nt * nt * 1024;
-  const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 8192));
-  KernelTimer timer(orientation ? "bias_tiles_k" : "bias_tiles_q", s);
-  hipLaunchKernelGGL((bias_tiles_kernel<uint16_t>), dim3(blocks), dim3(256), 0, s, p,
-                     static_cast<const uint16_t*>(bias), out, nt, orientation);
+  const int64_t blocks = static_cast<int64_t>(p.H) * nt * nt;
+  KernelTimer timer(out_k ? "bias_tiles_qk" : "bias_tiles_q", s);
+  hipLaunchKernelGGL((bias_tiles_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p,
+                     static_cast<const uint16_t*>(bias), out_q, out_k, nt);
   return hipGetLastError();
 }
 

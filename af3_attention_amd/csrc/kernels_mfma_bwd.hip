@@ -40,8 +40,8 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restri
 
 // Per-row terms of the backward, one thread per (r, j, h) in memory order (so a
 // wave reads contiguous 2*d-byte pieces of O and dO):
-//   delta[r,h,j] = sum_c dout[r,j,h,c] o[r,j,h,c]
-//   qaug[r,h,j]  = the query-side split operands of -sqrt(d) lse and -delta
+//   qaug[r,h,j]  = the query-side split operands of -sqrt(d) lse and of -D,
+//                  D = sum_c dout[r,j,h,c] o[r,j,h,c]
 //   kaug[r,j]    = the key-side split operands of sqrt(d) mask (threads with h = 0)
 // (layouts of the operands: pipe_common.h).
 template <int D>
@@ -68,7 +68,6 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(Problem p, BwdArgs a)
     }
   }
   const int64_t rhj = (static_cast<int64_t>(r) * p.H + h) * p.N + j;
-  a.delta[rhj] = s;
   const float sd = sqrtf(static_cast<float>(D));
   const Split3 na = split3(-lse_term(a.lse[rhj], sd, true));
   const Split3 nd = split3(-s);
@@ -97,8 +96,7 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_q, 
                        s, p, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = launch_bias_tiles(p, a.bias, bias_q, 0, s)) != hipSuccess) return e;
-  if ((e = launch_bias_tiles(p, a.bias, bias_k, 1, s)) != hipSuccess) return e;
+  if ((e = launch_bias_tiles(p, a.bias, bias_q, bias_k, s)) != hipSuccess) return e;
   if ((e = launch_dq_pipe(p, a, bias_q, s)) != hipSuccess) return e;
   if ((e = launch_dkdv_pipe(p, a, bias_k, s)) != hipSuccess) return e;
   if (a.dbias) {
@@ -118,23 +116,22 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_q, 
 size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdLayout {
-  size_t delta, qaug, kaug, bias, part, total;
+  size_t qaug, kaug, bias, part, total;
 };
 BwdLayout bwd_layout(const Problem& p) {
   BwdLayout l;
   const int groups = dbias_pipe_groups(p);
-  l.delta = align_up(static_cast<size_t>(p.R) * p.H * p.N * sizeof(float));
   l.qaug = align_up(static_cast<size_t>(p.R) * p.H * p.N * 16);
   l.kaug = align_up(static_cast<size_t>(p.R) * p.N * 16);
   l.bias = align_up(tiled_bias_bytes(p));
   l.part = groups > 1 ? align_up(static_cast<size_t>(groups) * p.H * p.N * p.N * sizeof(float)) : 0;
-  l.total = l.delta + l.qaug + l.kaug + 2 * l.bias + l.part;
+  l.total = l.qaug + l.kaug + 2 * l.bias + l.part;
   return l;
 }
 
 }  // namespace
 
-// Workspace: delta [R,H,N] fp32 | qaug [R,H,N] x 16 B | kaug [R,N] x 16 B |
+// Workspace: qaug [R,H,N] x 16 B | kaug [R,N] x 16 B |
 // tiled bias, query lanes | tiled bias, key lanes | dbias partials [G,H,N,N] fp32.
 size_t bwd_mfma_workspace_bytes(const Problem& p) { return bwd_layout(p).total; }
 
@@ -143,8 +140,7 @@ hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& args, void* ws, hipS
   const int groups = dbias_pipe_groups(p);
   char* base = static_cast<char*>(ws);
   BwdArgs a = args;
-  a.delta = reinterpret_cast<float*>(base);
-  base += l.delta;
+  a.delta = nullptr;  // D lives in qaug on this path
   a.qaug = base;
   base += l.qaug;
   a.kaug = base;

@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void fwd_pipe_kernel(Problem p, FwdArgs a, 
 
 template <int D>
 hipError_t fwd_pipe_dispatch(const Problem& p, const FwdArgs& a, float* bias_t, hipStream_t s) {
-  hipError_t e = launch_bias_tiles(p, a.bias, bias_t, 0, s);
+  hipError_t e = launch_bias_tiles(p, a.bias, bias_t, nullptr, s);
   if (e != hipSuccess) return e;
   const int64_t blocks = static_cast<int64_t>((p.N + kFwdQueries - 1) / kFwdQueries) * p.H *
                          ((p.R + kFwdRows - 1) / kFwdRows);

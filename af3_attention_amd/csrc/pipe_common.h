@@ -285,8 +285,9 @@ __device__ __forceinline__ f32x16 load_bias_tile(const float* __restrict__ tile,
 // Number of 32-wide tiles per axis of the tiled bias (positions padded to 128).
 inline int bias_tiles(int n) { return (n + 127) / 128 * 4; }
 size_t tiled_bias_bytes(const Problem& p);
-// Writes the tiled, sqrt(d)-scaled fp32 bias (orientation 0 or 1, see above).
-hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out, int orientation, hipStream_t s);
+// Writes the tiled, sqrt(d)-scaled fp32 bias in the query-lane order to out_q and,
+// if out_k is not NULL, in the key-lane order to out_k (see above).
+hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out_q, float* out_k, hipStream_t s);
 
 }  // namespace evo
 

@@ -113,38 +113,32 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
       copy16_to_lds(uniform_ptr(qaug_row[0]), 0u, lds0 + DUMMY);
   };
 
-  // sqrt(d) * bias of the wave's keys for the two 32-query tiles of a block.
+  // sqrt(d) * bias of the wave's keys for 32-query tile t of block qb.
   const int kt = min(kb * (kKvKeys / 32) + wave, nt - 1);
-  auto load_bias = [&](f32x16 (&b)[2], int qb) {
-    b[0] = load_bias_tile(bias_k + bias_tile_offset(h, 2 * qb, kt, nt), lane);
-    b[1] = load_bias_tile(bias_k + bias_tile_offset(h, 2 * qb + 1, kt, nt), lane);
+  auto load_bias = [&](f32x16& b, int qb, int t) {
+    b = load_bias_tile(bias_k + bias_tile_offset(h, 2 * qb + t, kt, nt), lane);
   };
-  f32x16 bias_reg[2][2];  // block qb uses set qb % 2
+  // One register tile per query tile: tile t of block qb + 1 is loaded as soon as
+  // both rows of block qb have used tile t.
+  f32x16 bias[2];
 
   auto step = [&](int qb, auto stage_c) {
     constexpr int s = decltype(stage_c)::value;
-    // Block qb's copies were the last memory operations issued (at the start of
-    // the previous block, after its bias loads).
+    // Block qb's copies and bias tiles were the last memory operations issued.
     wait_vmcnt<0>();
     barrier();
-    // Start block qb + 1 at once: its bias into the other register set, then its
-    // copies into the other buffer (read during the previous block).  Issued in
-    // this order, the compiler's wait for this block's bias (below) leaves the
-    // copies in flight.
-    if (qb + 1 < nqb) {
-      load_bias(bias_reg[s ^ 1], qb + 1);
-      issue_block(qb + 1, std::integral_constant<int, s ^ 1>());
-    }
+    // Start block qb + 1's copies at once into the other buffer (read during the
+    // previous block).
+    if (qb + 1 < nqb) issue_block(qb + 1, std::integral_constant<int, s ^ 1>());
     if (!wave_active) return;
-    f32x16 (&bias)[2] = bias_reg[s];
     const uint32_t st = lds0 + s * STAGE;
 
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const uint32_t tq = st + (2 * i) * TB, tdo = st + (2 * i + 1) * TB;
-      const uint32_t qaug_lds = st + NT * TB + i * kBlk * 16;
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int i = 0; i < RW; ++i) {
+        const uint32_t tq = st + (2 * i) * TB, tdo = st + (2 * i + 1) * TB;
+        const uint32_t qaug_lds = st + NT * TB + i * kBlk * 16;
         const int jl = t * 32 + (lane & 31);
         const u32x4 qa = lds_load16(qaug_lds + jl * 16);
         const u32x4 s_q = qb * kBlk + jl < p.N ? u32x4{qa[0], qa[1], kBf16One | (kBf16One << 16), 0u}
@@ -154,6 +148,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tq, t * 32, ks, lane), kop[i][ks], sacc);
         sacc = mma(s_q, s_key[i], sacc);
+        // (the last block reloads its own tiles: a harmless, branch-free extra load)
+        if (i == RW - 1) load_bias(bias[t], min(qb + 1, nqb - 1), t);
         f32x16 dp = mma(rd.rows_operand(tdo, t * 32, 0, lane), vop[i][0], f32x16{});
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tdo, t * 32, ks, lane), vop[i][ks], dp);
@@ -184,7 +180,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
     }
   };
 
-  load_bias(bias_reg[0], 0);
+  load_bias(bias[0], 0, 0);
+  load_bias(bias[1], 0, 1);
   issue_block(0, std::integral_constant<int, 0>());
   for (int qb = 0; qb < nqb; qb += 2) {
     step(qb, std::integral_constant<int, 0>());

@@ -39,6 +39,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, const float* __restrict__ bias_q,
                                                          int nt) {
   constexpr int kDqRows = dq_rows<D>();
+  // Software-pipelined units where the registers allow it (not at d = 64).
+  constexpr bool kPipelined = D <= 32;
   constexpr int TB = Tile<D>::BYTES;                    // 64 keys
   constexpr int NT = 2 * kDqRows;                       // K, V of each row
   constexpr int STAGE = NT * TB + kDqRows * kBlk * 16;  // + key-side operands
@@ -113,66 +115,122 @@ __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, c
       copy16_to_lds(uniform_ptr(kaug_row[0]), 0u, lds0 + DUMMY);
   };
 
-  // sqrt(d) * bias^T of the wave's queries for the two 32-key tiles of a block.
+  // sqrt(d) * bias^T of the wave's queries for 32-key tile mb of block kb.
   const int qt = min(qb * (kDqQueries / 32) + wave, nt - 1);
-  auto load_bias = [&](f32x16 (&b)[2], int kb) {
-    b[0] = load_bias_tile(bias_q + bias_tile_offset(h, qt, 2 * kb, nt), lane);
-    b[1] = load_bias_tile(bias_q + bias_tile_offset(h, qt, 2 * kb + 1, nt), lane);
+  auto load_bias = [&](f32x16& b, int kb, int mb) {
+    b = load_bias_tile(bias_q + bias_tile_offset(h, qt, 2 * kb + mb, nt), lane);
   };
-  f32x16 bias_reg[2][2];  // block kb uses set kb % 2
+  // One register tile per key tile: tile mb of block kb + 1 is loaded as soon as
+  // every row of block kb has used tile mb.
+  f32x16 bias[2];
+
+  // A block is U = 2 * kDqRows units (key tile mb = u / kDqRows, row i = u % kDqRows),
+  // each in three phases: A = LDS operand reads and the S^T, dP^T MFMAs; B = the
+  // vector work giving dS^T; C = the dQ^T MFMAs.  Unit u's B and C phases run
+  // beside unit u + 1's A phase, with LDS reads one unit further ahead; the
+  // scheduling barriers keep each unit's group in this order.
+  constexpr int U = 2 * kDqRows;
+  struct AOps {
+    u32x4 k[KS], v[KS], kaug;
+  };
+  struct COps {
+    u32x4 kt[DB][2];
+  };
+  auto load_a = [&](AOps& o, uint32_t st, int u) {
+    const int mb = u / kDqRows, i = u % kDqRows;
+    const uint32_t tk = st + (2 * i) * TB, tv = st + (2 * i + 1) * TB;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      o.k[ks] = rd.rows_operand(tk, mb * 32, ks, lane);
+      o.v[ks] = rd.rows_operand(tv, mb * 32, ks, lane);
+    }
+    o.kaug = lds_load16(st + NT * TB + i * kBlk * 16 + (mb * 32 + (lane & 31)) * 16);
+  };
+  auto load_c = [&](COps& o, uint32_t st, int u) {
+    const int mb = u / kDqRows, i = u % kDqRows;
+    const uint32_t tk = st + (2 * i) * TB;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) o.kt[db][t] = rd.tr_operand(tk, db, mb * 32, t);
+  };
+  auto phase_a = [&](const AOps& o, int kb, int u, f32x16& sacc, f32x16& dp) {
+    const int mb = u / kDqRows, i = u % kDqRows;
+    const u32x4 s_key = half ? u32x4{0u, 0u, 0u, 0u} : o.kaug;
+    sacc = mma(o.k[0], qop[i][0], bias[mb]);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) sacc = mma(o.k[ks], qop[i][ks], sacc);
+    sacc = mma(s_key, s_q[i], sacc);
+    // (the last block reloads its own tile: a harmless, branch-free extra load)
+    if (i == kDqRows - 1) load_bias(bias[mb], min(kb + 1, nkb - 1), mb);
+    dp = mma(o.v[0], doop[i][0], f32x16{});
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) dp = mma(o.v[ks], doop[i][ks], dp);
+    dp = mma(dp_key, dp_q[i], dp);
+  };
+  auto phase_bc = [&](const COps& o, int u, const f32x16& sacc, const f32x16& dp) {
+    const int i = u % kDqRows;
+    u32x4 dsb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float dsv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsv[e] = fast_exp2(sacc[8 * t + e] * c1) * dp[8 * t + e];
+      dsb[t] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                     pack_bf16(dsv[6], dsv[7])};
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) dq_acc[i][db] = mma(o.kt[db][t], dsb[t], dq_acc[i][db]);
+  };
 
   auto step = [&](int kb, auto stage_c) {
     constexpr int s = decltype(stage_c)::value;
-    // Block kb's copies were the last memory operations issued (at the start of
-    // the previous block, after its bias loads).
+    // Block kb's copies and bias tiles were the last memory operations issued.
     wait_vmcnt<0>();
     barrier();
-    // Start block kb + 1 at once: its bias into the other register set, then its
-    // copies into the other buffer (read during the previous block).
-    if (kb + 1 < nkb) {
-      load_bias(bias_reg[s ^ 1], kb + 1);
-      issue_block(kb + 1, std::integral_constant<int, s ^ 1>());
-    }
+    // Start block kb + 1's copies at once into the other buffer (read during the
+    // previous block).
+    if (kb + 1 < nkb) issue_block(kb + 1, std::integral_constant<int, s ^ 1>());
     if (!wave_active) return;
-    f32x16 (&bias)[2] = bias_reg[s];
     const uint32_t st = lds0 + s * STAGE;
 
+    if constexpr (kPipelined) {
+      AOps ao[2];
+      COps co[2];
+      f32x16 sacc[2], dp[2];
+      load_a(ao[0], st, 0);
+      load_c(co[0], st, 0);
+      if (U > 1) load_a(ao[1], st, 1);
+      phase_a(ao[0], kb, 0, sacc[0], dp[0]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kDqRows; ++i) {
-      const uint32_t tk = st + (2 * i) * TB, tv = st + (2 * i + 1) * TB;
-      const uint32_t kaug_lds = st + NT * TB + i * kBlk * 16;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        u32x4 s_key = lds_load16(kaug_lds + (mb * 32 + (lane & 31)) * 16);
-        if (half) s_key = u32x4{0u, 0u, 0u, 0u};
-        f32x16 sacc = mma(rd.rows_operand(tk, mb * 32, 0, lane), qop[i][0], bias[mb]);
-#pragma unroll
-        for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tk, mb * 32, ks, lane), qop[i][ks], sacc);
-        sacc = mma(s_key, s_q[i], sacc);
-        f32x16 dp = mma(rd.rows_operand(tv, mb * 32, 0, lane), doop[i][0], f32x16{});
-#pragma unroll
-        for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tv, mb * 32, ks, lane), doop[i][ks], dp);
-        dp = mma(dp_key, dp_q[i], dp);
-
-        u32x4 dsb[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float dsv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dsv[e] = fast_exp2(sacc[8 * u + e] * c1) * dp[8 * u + e];
-          dsb[u] = u32x4{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
-                         pack_bf16(dsv[6], dsv[7])};
+      for (int u = 0; u < U; ++u) {
+        if (u + 1 < U) {
+          load_c(co[(u + 1) & 1], st, u + 1);
+          if (u + 2 < U) load_a(ao[u & 1], st, u + 2);
+          phase_a(ao[(u + 1) & 1], kb, u + 1, sacc[(u + 1) & 1], dp[(u + 1) & 1]);
         }
+        phase_bc(co[u & 1], u, sacc[u & 1], dp[u & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            dq_acc[i][db] = mma(rd.tr_operand(tk, db, mb * 32, u), dsb[u], dq_acc[i][db]);
+      for (int u = 0; u < U; ++u) {
+        AOps ao;
+        COps co;
+        f32x16 sacc, dp;
+        load_a(ao, st, u);
+        phase_a(ao, kb, u, sacc, dp);
+        load_c(co, st, u);
+        phase_bc(co, u, sacc, dp);
       }
     }
   };
 
-  load_bias(bias_reg[0], 0);
+  load_bias(bias[0], 0, 0);
+  load_bias(bias[1], 0, 1);
   issue_block(0, std::integral_constant<int, 0>());
   for (int kb = 0; kb < nkb; kb += 2) {
     step(kb, std::integral_constant<int, 0>());

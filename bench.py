@@ -14,7 +14,10 @@ Prints one JSON line.  Besides the throughput it reports
   roofline      the kernel with the largest share of the step: algorithmic
                 flops (or bytes) per launch divided by its mean launch time,
                 measured with HIP events recorded by the library on the launch
-                stream inside the timed region, against the MI355X peak;
+                stream during a second timed pass of the same steps (the first
+                pass, which gives the throughput, runs without them), against
+                the MI355X peak; traffic is the HBM bytes per launch from the
+                committed counter record, while the kernel's sources match it;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores on a bounded
                 sample of rows of the same workload (skip with --no-cpu-baseline).
 """
@@ -49,16 +52,70 @@ KERNEL_FLOP_FACTOR = {
 }
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "af3_attention_amd", "csrc")
+# The source files each timed kernel is compiled from: a traffic record counts only
+# while these are unchanged since its counters were taken.
+COMMON_SOURCES = ["evoattn_internal.h", "mfma_common.h", "pipe_common.h"]
+KERNEL_SOURCES = {
+    "fwd_mfma": ["kernels_mfma_fwd.hip"],
+    "bwd_dkdv_mfma": ["kernels_bwd_dkdv.hip"],
+    "bwd_dq_mfma": ["kernels_bwd_dq.hip"],
+    "bwd_dbias_mfma": ["kernels_bwd_dbias.hip"],
+}
+
+
+def sources_digest(kernel):
+    """sha256 (first 16 hex digits) over the kernel's source files, or None."""
+    import hashlib
+
+    if kernel not in KERNEL_SOURCES:
+        return None
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch (fetch + write) from the committed counter record.
+
+    profiles/hbm_traffic_<workload>.md holds one line per kernel,
+    "record: kernel=<name> fetch_bytes=<B> write_bytes=<B> sources=<digest>",
+    written from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) scaled by
+    the copy calibration.  Returns None when there is no record for the kernel or
+    its sources have changed since.
+    """
+    path = os.path.join(HERE, "profiles", f"hbm_traffic_{workload}.md")
+    digest = sources_digest(kernel)
+    if digest is None or not os.path.exists(path):
+        return None
+    for line in open(path):
+        if not line.startswith("record:"):
+            continue
+        kv = dict(x.split("=", 1) for x in line[len("record:"):].split())
+        if kv.get("kernel") == kernel and kv.get("sources") == digest:
+            return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first (the GPU clocks take some tens of ms to settle)")
     ap.add_argument("--workload", default="tri_start_bf16_n384")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain 256 MiB device copy three times "
+                         "(the reference kernel that scales HBM byte counters)")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the second pass with per-kernel HIP events (no roofline)")
     return ap.parse_args()
 
 
@@ -79,12 +136,25 @@ def cpu_baseline(w, inp, target_s):
         oracle.bwd(q, k, v, b, m, do, t, rows=rows)
         return time.perf_counter() - t0
 
+    # Size the sample from a one-row probe, then once more from the first sample
+    # if that fell well short of the target (the probe carries start-up costs).
     probe = run([0])
-    nrows = int(max(1, min(w.rows, target_s / max(probe, 1e-6))))
-    rows = list(range(nrows))
-    secs = run(rows) if nrows > 1 else probe
+    nrows, secs = 1, probe
+    for _ in range(2):
+        if secs >= 0.6 * target_s or nrows >= w.rows:
+            break
+        nrows = int(max(1, min(w.rows, nrows * target_s / max(secs, 1e-6))))
+        secs = run(list(range(nrows)))
+    # A host fast enough to finish every row early repeats the whole workload.
+    reps = 1
+    if nrows >= w.rows and secs < 0.6 * target_s:
+        reps = int(min(8, max(2, round(target_s / max(secs, 1e-6)))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            run(list(range(nrows)))
+        secs = time.perf_counter() - t0
     per_row_flops = 14.0 * w.n * w.n * w.heads * w.head_dim
-    value = per_row_flops * nrows / secs / 1e12
+    value = per_row_flops * nrows * reps / secs / 1e12
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -95,7 +165,8 @@ def cpu_baseline(w, inp, target_s):
         pass
     return {
         "value": value, "unit": UNIT, "cores": used, "kind": "oracle",
-        "sample": f"rows 0..{nrows - 1} of {w.rows} of {w.name} (fwd+bwd, fp64), {secs:.2f} s",
+        "sample": f"rows 0..{nrows - 1} of {w.rows} of {w.name} (fwd+bwd, fp64)"
+                  + (f" x {reps} passes" if reps > 1 else "") + f", {secs:.2f} s",
         "seconds": secs, "cpu_model": cpu_model,
     }
 
@@ -135,19 +206,28 @@ def main():
     base_mem = torch.cuda.memory_allocated(dev)
 
     stream = torch.cuda.current_stream(dev)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    _lib.timing_collect()          # drop anything recorded before
-    _lib.timing_enable(True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    _lib.timing_enable(False)
-    kernels = _lib.timing_collect()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
+
+    def timed(kernel_timing):
+        """Time exactly args.steps steps; returns (ms per step, per-kernel records)."""
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        _lib.timing_collect()  # drop anything recorded before
+        _lib.timing_enable(kernel_timing)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        _lib.timing_enable(False)
+        return start.elapsed_time(stop) / args.steps, _lib.timing_collect()
+
+    # The throughput pass runs without per-kernel events (each launch would gain
+    # two event records, a few microseconds of gap); a second pass of the same
+    # steps records them, for the roofline of the dominant kernel.
+    ms_per_step, _ = timed(False)
+    kernels = {}
+    if not args.no_kernel_timing:
+        events_ms_per_step, kernels = timed(True)
     peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem
 
     flops_step = w.flops_fwd_bwd() * len(variants)
@@ -166,8 +246,23 @@ def main():
             achieved = factor * units / (avg_ms * 1e-3) / 1e12
             peak = PEAK_BF16_MFMA_TFLOPS if bound == "mfma" else PEAK_FP32_VECTOR_TFLOPS
             roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                        "frac": achieved / peak, "traffic": None, "kernel": name,
+                        "frac": achieved / peak, "traffic": recorded_traffic(name, w.name), "kernel": name,
                         "avg_launch_ms": avg_ms, "launches": count}
+
+    calibration = None
+    if args.copy_calibration:
+        # An elementwise kernel that reads and writes exactly `nbytes` each (negation
+        # of a contiguous fp32 tensor): its FETCH_SIZE and WRITE_SIZE readings give
+        # the factor between counter bytes and true HBM bytes.
+        nbytes = 256 << 20
+        src = torch.randn(nbytes // 4, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        calibration = {"kernel": "torch.neg fp32", "read_bytes": nbytes, "write_bytes": nbytes, "launches": 3}
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -183,8 +278,11 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_ms_per_step": {k: tot / args.steps for k, (c, tot) in kernels.items()},
+        "events_pass_ms_per_step": None if args.no_kernel_timing else events_ms_per_step,
         "peak_hbm_extra_bytes": int(peak_extra),
     }
+    if calibration:
+        line["copy_calibration"] = calibration
     print(json.dumps(line), flush=True)
 
 

@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
     }
   };
 
-  // Prologue: rows r_begin .. r_begin + NS - 2 into stages 0 .. NS - 2.
+  // Prologue: the bias tiles have arrived, then rows r_begin .. r_begin + NS - 2
+  // go into stages 0 .. NS - 2.
+  retire(bias[0]);
+  retire(bias[1]);
   if (r_begin < r_end) issue_row(r_begin, std::integral_constant<int, 0>());
   if constexpr (NS > 2) {
     if (r_begin + 1 < r_end) issue_row(r_begin + 1, std::integral_constant<int, 1>());

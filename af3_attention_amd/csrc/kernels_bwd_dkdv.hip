@@ -127,6 +127,10 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
     // Block qb's copies and bias tiles were the last memory operations issued.
     wait_vmcnt<0>();
     barrier();
+    // (Tell the compiler the bias tiles have arrived, before the copies below:
+    // its own wait for them would otherwise also drain those copies.)
+    retire(bias[0]);
+    retire(bias[1]);
     // Start block qb + 1's copies at once into the other buffer (read during the
     // previous block).
     if (qb + 1 < nqb) issue_block(qb + 1, std::integral_constant<int, s ^ 1>());
@@ -180,6 +184,16 @@ __global__ __launch_bounds__(256, 2) void dkdv_pipe_kernel(Problem p, BwdArgs a,
     }
   };
 
+  // The operands loaded above have arrived before the loop issues its copies.
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      retire(kop[i][ks]);
+      retire(vop[i][ks]);
+    }
+    retire(s_key[i]);
+  }
   load_bias(bias[0], 0, 0);
   load_bias(bias[1], 0, 1);
   issue_block(0, std::integral_constant<int, 0>());

@@ -190,6 +190,10 @@ __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, c
     // Block kb's copies and bias tiles were the last memory operations issued.
     wait_vmcnt<0>();
     barrier();
+    // (Tell the compiler the bias tiles have arrived, before the copies below:
+    // its own wait for them would otherwise also drain those copies.)
+    retire(bias[0]);
+    retire(bias[1]);
     // Start block kb + 1's copies at once into the other buffer (read during the
     // previous block).
     if (kb + 1 < nkb) issue_block(kb + 1, std::integral_constant<int, s ^ 1>());
@@ -229,6 +233,17 @@ __global__ __launch_bounds__(256, 2) void dq_pipe_kernel(Problem p, BwdArgs a, c
     }
   };
 
+  // The operands loaded above have arrived before the loop issues its copies.
+#pragma unroll
+  for (int i = 0; i < kDqRows; ++i) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      retire(qop[i][ks]);
+      retire(doop[i][ks]);
+    }
+    retire(s_q[i]);
+    retire(dp_q[i]);
+  }
   load_bias(bias[0], 0, 0);
   load_bias(bias[1], 0, 1);
   issue_block(0, std::integral_constant<int, 0>());

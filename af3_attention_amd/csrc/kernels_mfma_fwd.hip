@@ -153,7 +153,12 @@ __global__ __launch_bounds__(256, 2) void fwd_pipe_kernel(Problem p, FwdArgs a, 
     dst[1] = load_bias_tile(btile + (2 * kb + 1) * 1024, lane);
   };
 
-  // Prologue: bias and stage of blocks 0 and 1, in the order of the loop body.
+  // Prologue: the query operands have arrived (so that no wait for them lands in
+  // the loop), then bias and stage of blocks 0 and 1, in the order of the loop body.
+#pragma unroll
+  for (int i = 0; i < kFwdRows; ++i)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) retire(qreg[i][ks]);
   load_bias(bias_reg[0], 0);
   issue_stage(0, std::integral_constant<int, 0>());
   if (nkb > 1) {
@@ -172,6 +177,11 @@ __global__ __launch_bounds__(256, 2) void fwd_pipe_kernel(Problem p, FwdArgs a, 
     else
       wait_vmcnt<0>();
     barrier();
+    // Tell the compiler this block's bias registers have arrived: its own wait for
+    // them, placed at their first use, would count only the loads it knows of and
+    // so also drain the copies in flight.
+    retire(bias_reg[st % 2][0]);
+    retire(bias_reg[st % 2][1]);
     uint32_t kt_lds[kFwdRows], vt_lds[kFwdRows];
 #pragma unroll
     for (int i = 0; i < kFwdRows; ++i) {

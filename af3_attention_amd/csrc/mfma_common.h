@@ -54,12 +54,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// max(a, b, c) in one v_max3_f32.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// max(a, b, c); the compiler fuses it into one v_max3_f32.  (Not inline asm: the
+// compiler's hazard checks do not see which registers an asm statement reads, so
+// an asm read of a fresh MFMA result could miss the required wait states.)
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // acc + lo(p) + hi(p) for a packed bf16 pair p, in one v_dot2_f32_bf16 with (1, 1).
 __device__ __forceinline__ float add_bf16_pair(uint32_t p, float acc) {

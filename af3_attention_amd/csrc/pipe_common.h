@@ -90,6 +90,17 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
   return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Makes the compiler wait here for the loads that produced x.  Registers loaded
+// before a loop that also issues the (compiler-invisible) direct copies would
+// otherwise be waited for inside the loop, with a count that also drains the
+// copies in flight.
+template <typename T>
+__device__ __forceinline__ void retire(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the host pass cannot place 512-bit operands)
+  asm volatile("" ::"v"(x));
+#endif
+}
+
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)(p)));
@@ -230,12 +241,30 @@ struct Stager {
       copy16_to_lds(uniform_ptr(base[0]), 0u, dummy);
       return;
     }
-    const int ti = tile_of<IT>(wave);
-    const char* b = base[0];
-#pragma unroll
-    for (int i = 1; i < NT; ++i)
-      if (ti == i) b = base[i];
     const uint32_t dst = lds + (IT * THREADS + wave * 64) * 16;
+    if constexpr (PER_TILE < 64) {
+      // A wave's 64 chunks span several tiles: per-lane tile and address.
+      const int lane = static_cast<int>(threadIdx.x & 63);
+      const int ti = (IT * THREADS + wave * 64 + lane) / PER_TILE;
+      const char* b = base[0];
+#pragma unroll
+      for (int i = 1; i < NT; ++i) b = ti == i ? base[i] : b;
+      int x, cbyte;
+      chunk_of(IT, wave, lane, x, cbyte);
+      const int pos = full ? x0 + x : min(x0 + x, n - 1);
+      copy16_to_lds(b + static_cast<size_t>(pos) * pstride + cbyte, dst);
+      return;
+    }
+    // Only tiles LO..HI can hold copy IT of some wave: select among those (a
+    // select over the whole array can end up as an indexed scratch access).
+    constexpr int LO = IT * THREADS / PER_TILE;
+    constexpr int HI = (IT * THREADS + THREADS - 64) / PER_TILE < NT - 1 ? (IT * THREADS + THREADS - 64) / PER_TILE
+                                                                         : NT - 1;
+    const int ti = tile_of<IT>(wave);
+    const char* b = base[LO];
+#pragma unroll
+    for (int i = LO + 1; i <= HI; ++i)
+      if (ti == i) b = base[i];
     if (full) {
       copy16_to_lds(uniform_ptr(b + static_cast<size_t>(x0) * pstride), voff[IT], dst);
     } else {

@@ -105,6 +105,25 @@ def test_large_logits_stay_finite():
     compare(gpu_fwd_bwd(inp), oracle_fwd_bwd(inp), "fp32")
 
 
+def test_bf16_softmax_reference_paths():
+    """bf16 path: rows whose first key block is masked, rows whose later logits
+    exceed the first block's by ~90 (the exact recompute path), fully masked rows."""
+    banner("bf16 softmax reference paths")
+    inp = generate(6, 200, 2, 32, dtype=torch.bfloat16, mask_kind="none", seed=12)
+    bias = inp["bias"].float()
+    bias[0, :, :32] = -90.0  # head 0: every query's first 32 keys far below the rest
+    inp["bias"] = bias.to(torch.bfloat16)
+    mask = torch.zeros(6, 200)
+    mask[1, :40] = float("-inf")  # first block dead, second partly
+    mask[2, :] = float("-inf")    # fully masked
+    mask[4, 150:] = float("-inf")
+    inp["mask"] = mask
+    got = gpu_fwd_bwd(inp)
+    compare(got, oracle_fwd_bwd(inp), "bf16")
+    assert torch.all(got["o"][2].float().cpu() == 0)
+    assert torch.all(torch.isneginf(got["lse"][2].cpu()))
+
+
 # ---------------------------------------------------------------- full sizes, sampled rows
 
 FULL = [

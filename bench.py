@@ -114,6 +114,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy three times "
                          "(the reference kernel that scales HBM byte counters)")
+    ap.add_argument("--memory-curve", action="store_true",
+                    help="instead of the throughput line: peak extra HBM of one fwd+bwd at N = 64 .. 1536 "
+                         "(R = N, H = 4, d = 32, bf16), beside a materialised fp32 torch reference until it "
+                         "runs out of memory")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the second pass with per-kernel HIP events (no roofline)")
     return ap.parse_args()
@@ -171,8 +175,68 @@ def cpu_baseline(w, inp, target_s):
     }
 
 
+def memory_curve():
+    """Peak HBM of one fwd + bwd versus N, for this library and a materialised reference.
+
+    The library keeps O(R*H*N + H*N^2) bytes besides its inputs and outputs.  The
+    reference forms the [R,H,N,N] scores, probabilities and their gradients in fp32
+    with torch autograd (fp32, because torch's bf16 batched products with transposed
+    operands are unsafe on this GPU) until it runs out of memory.
+    """
+    import torch
+    import af3_attention_amd as ea
+    from workloads import generate
+
+    dev = torch.device("cuda:0")
+    out = []
+    reference_alive = True
+    for n in (64, 128, 256, 384, 512, 768, 1024, 1536):
+        inp = generate(n, n, 4, 32, dtype=torch.bfloat16, bias_std=2 ** 0.5, mask_kind="tail_fixed",
+                       mask_frac=0.05, seed=0)
+        g = {x: (None if inp[x] is None else inp[x].to(dev)) for x in ("q", "k", "v", "bias", "mask", "dout")}
+        del inp
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        o, lse = ea.evoattn_fwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], False)
+        grads = ea.evoattn_bwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], o, lse, g["dout"], False)
+        torch.cuda.synchronize()
+        fused = torch.cuda.max_memory_allocated(dev) - base
+        del o, lse, grads
+        row = {"n": n, "rows": n, "inputs_bytes": base, "fused_peak_extra_bytes": fused}
+        if reference_alive:
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats(dev)
+            try:
+                q, k, v = (g[x].float().permute(0, 2, 1, 3).contiguous().requires_grad_() for x in ("q", "k", "v"))
+                bias = g["bias"].float().requires_grad_()
+                s = torch.matmul(q, k.transpose(-1, -2).contiguous()) / 32 ** 0.5 + bias[None] \
+                    + g["mask"][:, None, None, :]
+                o_ref = torch.matmul(torch.softmax(s, dim=-1), v)
+                o_ref.backward(g["dout"].float().permute(0, 2, 1, 3).contiguous())
+                torch.cuda.synchronize()
+                row["reference_peak_extra_bytes"] = torch.cuda.max_memory_allocated(dev) - base
+            except torch.cuda.OutOfMemoryError:
+                row["reference_peak_extra_bytes"] = "out of memory"
+                reference_alive = False
+            q = k = v = bias = s = o_ref = None
+            torch.cuda.empty_cache()
+        else:
+            row["reference_peak_extra_bytes"] = "not run (out of memory at a smaller N)"
+        out.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        del g
+    total = torch.cuda.get_device_properties(dev).total_memory
+    print(json.dumps({"memory_curve": out, "device_memory_bytes": total, "dtype": "bf16",
+                      "config": {"heads": 4, "head_dim": 32, "mask": "tail 5%"}}), flush=True)
+
+
 def main():
     args = parse()
+    if args.memory_curve and args.gpus == 1:
+        memory_curve()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -225,6 +289,20 @@ def main():
     # two event records, a few microseconds of gap); a second pass of the same
     # steps records them, for the roofline of the dominant kernel.
     ms_per_step, _ = timed(False)
+
+    # Forward alone (the same inputs, the same number of steps).
+    def fwd_only():
+        for inp in inputs:
+            ea.evoattn_fwd(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], bool(inp["transpose"]))
+
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for _ in range(args.steps):
+        fwd_only()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / args.steps
     kernels = {}
     if not args.no_kernel_timing:
         events_ms_per_step, kernels = timed(True)
@@ -275,6 +353,9 @@ def main():
         "config": {"workload": w.name, "rows": w.rows, "n": w.n, "heads": w.heads, "head_dim": w.head_dim,
                    "transpose": variants, "mask": w.mask_kind, "seed": args.seed},
         "frac_of_bf16_peak": value / PEAK_BF16_MFMA_TFLOPS,
+        "fwd_only": {"ms_per_step": fwd_ms, "tflops": w.flops_fwd() * len(variants) / (fwd_ms * 1e-3) / 1e12,
+                     "frac_of_bf16_peak": w.flops_fwd() * len(variants) / (fwd_ms * 1e-3) / 1e12
+                     / PEAK_BF16_MFMA_TFLOPS},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_ms_per_step": {k: tot / args.steps for k, (c, tot) in kernels.items()},

@@ -196,10 +196,22 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
 int dbias_pipe_groups(const Problem& p) {
   const int nb = (p.N + kDbT - 1) / kDbT;
   const int64_t tiles = static_cast<int64_t>(p.H) * nb * nb;
-  // About one full round of resident workgroups (one per CU on 256 CUs).
-  int64_t g = std::max<int64_t>(1, 256 / tiles);
-  g = std::min<int64_t>(g, p.R);
-  return static_cast<int>(g);
+  // One workgroup per CU at a time (256 CUs on MI355X): pick the number of row
+  // groups g <= 16 whose tiles * g workgroups fill the last round best (ties: the
+  // smallest g, which also keeps the partial sums and their reduction small).
+  constexpr int64_t kCus = 256;
+  int best = 1;
+  double best_eff = 0.0;
+  for (int g = 1; g <= 16 && g <= p.R; ++g) {
+    const int64_t wgs = tiles * g;
+    const double eff = static_cast<double>(wgs) / static_cast<double>(kCus * ((wgs + kCus - 1) / kCus));
+    if (eff > best_eff + 1e-3) {
+      best_eff = eff;
+      best = g;
+    }
+    if (eff >= 0.98) break;
+  }
+  return best;
 }
 
 hipError_t launch_dbias_pipe(const Problem& p, const BwdArgs& a, const float* bias_k, int groups, float* out,

@@ -137,3 +137,6 @@ def bwd(q, k, v, bias, mask, dout, transpose=0, rows=None):
     if rc != 0:
         raise RuntimeError(f"evo_oracle_bwd failed with code {rc}")
     return dq, dk, dv, dbias
+
+
+from .ln_proj import layer_norm, ln_proj_bwd, ln_proj_fwd  # noqa: E402,F401

@@ -153,3 +153,98 @@ def generate_workload(w: Workload, *, transpose: int | None = None, seed: int = 
     return generate(w.rows, w.n, w.heads, w.head_dim, dtype=w.torch_dtype, transpose=t,
                     bias_std=w.bias_std, mask_kind=w.mask_kind, mask_frac=w.mask_frac,
                     seed=seed, device=device)
+
+
+# ---------------------------------------------------------------- LayerNorm + projections
+
+@dataclass(frozen=True)
+class ProjWorkload:
+    """The fused layer norm + projection step that produces the attention inputs.
+
+    x is [A, B, c] (pair tensor: A = B = N, c = pair channels; MSA: A = S rows,
+    B = N, c = MSA channels).  With qkv, the projection writes q, k, v of
+    [A, B, H, d]; with bias (pair tensor only) it writes the pair bias [H, N, N]."""
+    name: str
+    a: int
+    b: int
+    channels: int
+    heads: int
+    head_dim: int
+    dtype: str
+    qkv: bool
+    bias: bool
+    bias_transpose: int = 0
+    desc: str = ""
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    @property
+    def tokens(self) -> int:
+        return self.a * self.b
+
+    @property
+    def outputs(self) -> int:
+        return (3 * self.heads * self.head_dim if self.qkv else 0) + (self.heads if self.bias else 0)
+
+
+PROJ_WORKLOADS = {
+    "pair_proj_fp32_n64": ProjWorkload(
+        "pair_proj_fp32_n64", 64, 64, 128, 4, 32, "fp32", True, True, 0,
+        "pair tensor N=64, c=128 -> q, k, v (H=4, d=32) and pair bias, fp32"),
+    # The step that feeds the headline attention workload (starting node, N=384).
+    "pair_proj_bf16_n384": ProjWorkload(
+        "pair_proj_bf16_n384", 384, 384, 128, 4, 32, "bf16", True, True, 0,
+        "pair tensor N=384, c=128 -> q, k, v (H=4, d=32) and pair bias, bf16"),
+    "pair_proj_end_bf16_n768": ProjWorkload(
+        "pair_proj_end_bf16_n768", 768, 768, 128, 4, 32, "bf16", True, True, 1,
+        "pair tensor N=768, c=128 -> q, k, v and the transposed pair bias (ending node), bf16"),
+    "msa_proj_bf16_s512_n384": ProjWorkload(
+        "msa_proj_bf16_s512_n384", 512, 384, 64, 8, 8, "bf16", True, False, 0,
+        "MSA tensor S=512 N=384, c=64 -> q, k, v (H=8, d=8), bf16"),
+}
+
+
+def generate_proj(a: int, b: int, channels: int, heads: int, head_dim: int, *, dtype=torch.bfloat16,
+                  qkv: bool = True, bias: bool = True, seed: int = 0, device="cpu"):
+    """Draw one seeded input set for layer norm + projections.
+
+    Draw order with one torch CPU generator: x, per-token scale, per-token
+    offset, gamma, beta, w_qkv, w_bias, dq, dk, dv, dbias.  Tokens get their own
+    offset (N(0,1)) and scale (exp of N(0, 0.5^2)) so the normalisation has
+    real work to do; gamma ~ 1 + N(0, 0.1^2), beta ~ N(0, 0.1^2) (fp32);
+    weights ~ N(0, 1/c) (fan-in scaling), cast to the compute dtype; upstream
+    gradients ~ N(0, 1) (dbias fp32, as the attention backward produces it)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    hd = heads * head_dim
+    x = torch.randn((a, b, channels), generator=gen, dtype=torch.float32)
+    scale = torch.exp(0.5 * torch.randn((a, b, 1), generator=gen, dtype=torch.float32))
+    offset = torch.randn((a, b, 1), generator=gen, dtype=torch.float32)
+    x = x * scale + offset
+    gamma = 1.0 + 0.1 * torch.randn(channels, generator=gen, dtype=torch.float32)
+    beta = 0.1 * torch.randn(channels, generator=gen, dtype=torch.float32)
+    w_qkv = torch.randn((3 * hd, channels), generator=gen, dtype=torch.float32) / math.sqrt(channels)
+    w_bias = torch.randn((heads, channels), generator=gen, dtype=torch.float32) / math.sqrt(channels)
+    grads = [torch.randn((a, b, heads, head_dim), generator=gen, dtype=torch.float32) for _ in range(3)]
+    dbias = torch.randn((heads, a, b), generator=gen, dtype=torch.float32)
+
+    def cast(t, dt=dtype):
+        return t.to(dt).to(device).contiguous()
+
+    return {
+        "x": cast(x), "gamma": cast(gamma, torch.float32), "beta": cast(beta, torch.float32),
+        "w_qkv": cast(w_qkv) if qkv else None, "w_bias": cast(w_bias) if bias else None,
+        "dq": cast(grads[0]) if qkv else None, "dk": cast(grads[1]) if qkv else None,
+        "dv": cast(grads[2]) if qkv else None,
+        "dbias": cast(dbias, torch.float32) if bias else None,
+        "eps": 1e-5, "heads": heads, "head_dim": head_dim,
+    }
+
+
+def generate_proj_workload(w: ProjWorkload, *, seed: int = 0, device="cpu"):
+    out = generate_proj(w.a, w.b, w.channels, w.heads, w.head_dim, dtype=w.torch_dtype,
+                        qkv=w.qkv, bias=w.bias, seed=seed, device=device)
+    out["bias_transpose"] = w.bias_transpose
+    return out

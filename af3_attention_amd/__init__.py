@@ -12,3 +12,4 @@ from .evoattn import (  # noqa: F401
     evoattn_fwd_workspace_bytes,
 )
 from ._lib import EvoAttnError, LIB_PATH  # noqa: F401
+from .evofusion import ln_proj_fwd  # noqa: F401,E402

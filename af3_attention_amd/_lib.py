@@ -16,6 +16,7 @@ EXPORTS = (
     "evoattn_bwd",
     "evoattn_timing_enable",
     "evoattn_timing_collect",
+    "evoattn_ln_proj_fwd",
 )
 
 _lib = None
@@ -49,6 +50,9 @@ def load():
     lib.evoattn_bwd.argtypes = [i64, i64, i64, i64, c_int, c_int,
                                 vp, vp, vp, vp, fp, vp, fp, vp, vp, vp, vp, fp, vp, sz, vp]
     lib.evoattn_bwd.restype = c_int
+    lib.evoattn_ln_proj_fwd.argtypes = [i64, i64, i64, i64, i64, c_int, c_int, ctypes.c_float,
+                                        vp, fp, fp, vp, vp, vp, vp, vp, vp, fp, fp, vp]
+    lib.evoattn_ln_proj_fwd.restype = c_int
     lib.evoattn_timing_enable.argtypes = [c_int]
     lib.evoattn_timing_enable.restype = None
     lib.evoattn_timing_collect.argtypes = [c_int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),

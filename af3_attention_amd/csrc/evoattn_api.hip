@@ -1,12 +1,14 @@
 // C entry points of the EvoAttention library: argument validation, workspace
 // layout and kernel dispatch.  Declared in include/evoattn.h.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
 
 #include "evoattn.h"
+#include "evofusion.h"
 #include "evoattn_internal.h"
 
 namespace {
@@ -88,6 +90,49 @@ size_t bwd_ws_bytes(const evo::Problem& p) {
   if (use_mfma(p)) return round_up(evo::bwd_mfma_workspace_bytes(p));
   const size_t delta = static_cast<size_t>(p.R) * p.H * p.N * sizeof(float);
   return round_up(delta);
+}
+
+// Validates the layer norm + projection problem; fills `p`.
+evoattn_status_t check_proj(int64_t A, int64_t B, int64_t C, int64_t heads, int64_t head_dim, int dtype,
+                            int bias_transpose, float eps, bool with_qkv, bool with_bias, evo::ProjProblem* p) {
+  if (A < 1 || B < 1 || C < 1 || heads < 1 || head_dim < 1)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (a=%lld b=%lld channels=%lld heads=%lld head_dim=%lld)",
+                (long long)A, (long long)B, (long long)C, (long long)heads, (long long)head_dim);
+  if (dtype != EVOATTN_FP32 && dtype != EVOATTN_BF16)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "dtype %d is not EVOATTN_FP32 or EVOATTN_BF16", dtype);
+  if (bias_transpose != 0 && bias_transpose != 1)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "bias_transpose must be 0 or 1, got %d", bias_transpose);
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0, got %g", (double)eps);
+  if (!with_qkv && !with_bias)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "w_qkv and w_bias are both NULL: nothing to project");
+  if (head_dim != 8 && head_dim != 16 && head_dim != 32 && head_dim != 64)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (8, 16, 32, 64)", (long long)head_dim);
+  if (C < 16 || C > 2048 || C % 8 != 0)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "channels %lld not supported (a multiple of 8 in 16..2048)", (long long)C);
+  if (with_bias && A != B)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "the pair bias needs a square token grid, got a=%lld b=%lld",
+                (long long)A, (long long)B);
+  const double T = static_cast<double>(A) * B;
+  const double widest = std::max(static_cast<double>(C), 3.0 * heads * head_dim);
+  if (T >= 2147483648.0 || T * widest >= 2147483648.0 || heads * head_dim * 3 >= 65536)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "problem too large: tokens=%.0f, widest row=%.0f", T, widest);
+  if (p) {
+    p->A = static_cast<int>(A);
+    p->B = static_cast<int>(B);
+    p->C = static_cast<int>(C);
+    p->H = static_cast<int>(heads);
+    p->D = static_cast<int>(head_dim);
+    p->T = A * B;
+    p->dtype = dtype;
+    p->bias_transpose = bias_transpose;
+    p->n_qkv = with_qkv ? static_cast<int>(3 * heads * head_dim) : 0;
+    p->n_out = p->n_qkv + (with_bias ? static_cast<int>(heads) : 0);
+    p->col_tiles = (with_bias && bias_transpose) ? 1 : 0;
+    p->tiles = p->col_tiles ? static_cast<int>(((A + 31) / 32) * B) : static_cast<int>((A * B + 31) / 32);
+    p->eps = eps;
+  }
+  return EVOATTN_OK;
 }
 
 }  // namespace
@@ -184,6 +229,44 @@ evoattn_status_t evoattn_bwd(int64_t rows, int64_t n, int64_t heads, int64_t hea
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = use_mfma(p) ? evo::launch_bwd_mfma(p, a, workspace, s) : evo::launch_bwd_vector(p, a, s);
   if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return EVOATTN_OK;
+}
+
+evoattn_status_t evoattn_ln_proj_fwd(int64_t a, int64_t b, int64_t channels, int64_t heads, int64_t head_dim,
+                                     int dtype, int bias_transpose, float eps, const void* x, const float* gamma,
+                                     const float* beta, const void* w_qkv, const void* w_bias, void* q, void* k,
+                                     void* v, void* bias, float* mean, float* rstd, void* stream) {
+  evo::ProjProblem p;
+  evoattn_status_t st = check_proj(a, b, channels, heads, head_dim, dtype, bias_transpose, eps, w_qkv != nullptr,
+                                   w_bias != nullptr, &p);
+  if (st != EVOATTN_OK) return st;
+  REQUIRE_PTR(x, 16);
+  REQUIRE_PTR(gamma, 4);
+  REQUIRE_PTR(beta, 4);
+  if (w_qkv) {
+    REQUIRE_PTR(w_qkv, 16);
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(k, 16);
+    REQUIRE_PTR(v, 16);
+  } else if (q || k || v) {
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "q, k, v must be NULL when w_qkv is NULL");
+  }
+  if (w_bias) {
+    REQUIRE_PTR(w_bias, 16);
+    REQUIRE_PTR(bias, 16);
+  } else if (bias) {
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "bias must be NULL when w_bias is NULL");
+  }
+  if ((mean == nullptr) != (rstd == nullptr))
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "mean and rstd must both be given or both be NULL");
+  OPTIONAL_PTR(mean, 4);
+  OPTIONAL_PTR(rstd, 4);
+  if ((st = check_device()) != EVOATTN_OK) return st;
+
+  evo::ProjFwdArgs args{x, gamma, beta, w_qkv, w_bias, q, k, v, bias, mean, rstd};
+  hipError_t e = evo::launch_ln_proj_fwd(p, args, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "layer norm + projection launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return EVOATTN_OK;
 }

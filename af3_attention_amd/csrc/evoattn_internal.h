@@ -85,6 +85,37 @@ int dbias_pipe_groups(const Problem& p);
 hipError_t launch_dbias_pipe(const Problem& p, const BwdArgs& a, const float* bias_k, int groups, float* out,
                              hipStream_t s);
 
+// Layer norm + projections of a token tensor x [A, B, C] into the attention's
+// inputs (kernels_ln_proj.hip).  Output row o < n_qkv goes to q (o < H*D), k
+// or v at [token][o % (H*D)]; rows n_qkv <= o < n_out are the pair-bias heads.
+struct ProjProblem {
+  int A, B, C, H, D;
+  int64_t T;           // tokens A*B
+  int dtype;           // 0 fp32, 1 bf16
+  int bias_transpose;  // bias[h][a][b] from token (b, a) instead of (a, b)
+  int n_qkv;           // 3*H*D, or 0 without q/k/v
+  int n_out;           // n_qkv + (H with bias, else 0)
+  int col_tiles;       // 32-token tiles run down a column of the A x B grid
+  int tiles;           // number of 32-token tiles
+  float eps;
+};
+
+struct ProjFwdArgs {
+  const void* x;
+  const float* gamma;
+  const float* beta;
+  const void* w_qkv;   // [n_qkv][C] or nullptr
+  const void* w_bias;  // [H][C] or nullptr
+  void* q;
+  void* k;
+  void* v;
+  void* bias;          // [H][A][B] or nullptr
+  float* mean;         // [T] or nullptr
+  float* rstd;         // [T] or nullptr
+};
+
+hipError_t launch_ln_proj_fwd(const ProjProblem& p, const ProjFwdArgs& a, hipStream_t s);
+
 // bf16 storage conversions (round to nearest even; NaN stays NaN).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -1,0 +1,76 @@
+/*
+ * evofusion.h -- C ABI of the fused layer norm + projections that produce the
+ * inputs of EvoAttention (evoattn.h), in the same library (libevoattn.so).
+ *
+ * The operation (MegaFold, gist.science technical summary, Methodik section 3
+ * "EvoFusion": layer normalisation and the linear projections after it are one
+ * operator whose inner loops are restructured so that the normalised tensor is
+ * never written to HBM between the two; the pages give no formulas, so this is
+ * the textbook layer norm followed by bias-free projections).  For every token
+ * t = (a, b) of x [A, B, C]:
+ *
+ *   mean[t] = (1/C) sum_c x[t,c]
+ *   rstd[t] = 1 / sqrt((1/C) sum_c (x[t,c] - mean[t])^2 + eps)   (biased variance)
+ *   y[t,c]  = (x[t,c] - mean[t]) * rstd[t] * gamma[c] + beta[c]
+ *   q[a,b,h,e] = sum_c y[t,c] w_qkv[h*d + e, c]
+ *   k[a,b,h,e] = sum_c y[t,c] w_qkv[H*d + h*d + e, c]
+ *   v[a,b,h,e] = sum_c y[t,c] w_qkv[2*H*d + h*d + e, c]
+ *   bias[h,a,b] = sum_c y[(a,b),c] w_bias[h,c]     bias_transpose == 0
+ *   bias[h,a,b] = sum_c y[(b,a),c] w_bias[h,c]     bias_transpose == 1
+ *
+ * q, k, v keep x's token order: for a pair tensor z [N, N, C] they are the
+ * attention's [R, N, H, d] inputs for the starting node (transpose = 0 in
+ * evoattn_fwd) and its [N, R, H, d] inputs for the ending node (transpose = 1).
+ * The bias is [H, N, N] in the attention's kernel frame: bias_transpose = 0 for
+ * the starting node, 1 for the ending node (whose query is the pair tensor's
+ * column index).  For MSA row attention, project the MSA tensor with w_bias =
+ * NULL and the pair tensor with w_qkv = NULL.
+ *
+ * ---------------------------------------------------------------- layouts
+ * Dense, row-major.  x [A][B][C]; w_qkv [3*H*d][C] (the layout of a torch
+ * Linear weight); w_bias [H][C]; q, k, v [A][B][H][d]; bias [H][A][B];
+ * gamma, beta [C] fp32; mean, rstd [A*B] fp32.
+ * dtype EVOATTN_BF16: x, w_qkv, w_bias, q, k, v, bias are bfloat16; the
+ *   statistics and every sum are fp32, and y is rounded to bf16 before the
+ *   projections (what an unfused bf16 pipeline stores between the two).
+ * dtype EVOATTN_FP32: the same arrays are float.
+ *
+ * ---------------------------------------------------------------- ownership
+ * Every pointer except `stream` is a device pointer owned by the caller.  The
+ * library allocates nothing; outputs are overwritten; inputs and outputs must
+ * not overlap.  Work is enqueued on `stream` (NULL = default stream).
+ *
+ * ---------------------------------------------------------------- errors
+ * Arguments are validated before anything is enqueued; the return value is an
+ * evoattn_status_t and evoattn_last_error_detail() describes a failure.
+ *
+ * Supported: A, B, H >= 1; d in {8, 16, 32, 64}; 16 <= C <= 2048 with C a
+ * multiple of 8; A*B < 2^31 and A*B*max(C, 3*H*d) < 2^31 elements; with
+ * w_bias, A == B.  Pointers 16-byte aligned (gamma, beta, mean, rstd: 4).
+ * The bf16 MFMA kernel covers C in {32, 64, 128} when the weights fit in
+ * LDS; other shapes run a vector-ALU kernel with the same results.
+ */
+#ifndef EVOFUSION_H
+#define EVOFUSION_H
+
+#include "evoattn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Forward.  w_qkv and w_bias may each be NULL (not both); q, k, v must be
+ * non-NULL exactly when w_qkv is, bias exactly when w_bias is.  mean and rstd
+ * (both or neither) receive the per-token statistics the backward needs. */
+evoattn_status_t evoattn_ln_proj_fwd(int64_t a, int64_t b, int64_t channels, int64_t heads,
+                                     int64_t head_dim, int dtype, int bias_transpose, float eps,
+                                     const void* x, const float* gamma, const float* beta,
+                                     const void* w_qkv, const void* w_bias,
+                                     void* q, void* k, void* v, void* bias,
+                                     float* mean, float* rstd, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EVOFUSION_H */

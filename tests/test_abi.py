@@ -11,20 +11,21 @@ import torch
 from af3_attention_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "evoattn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("evoattn.h", "evofusion.h")]
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, DEVICE = 0, 1, 2, 3, 4
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(evoattn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "evoattn.h"\nint main(void){return evoattn_abi_version() == EVOATTN_ABI_VERSION ? 0 : 1;}\n')
+    src.write_text('#include "evoattn.h"\n#include "evofusion.h"\n'
+                   'int main(void){return evoattn_abi_version() == EVOATTN_ABI_VERSION ? 0 : 1;}\n')
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
                     str(src)], check=True)
 
@@ -151,3 +152,58 @@ def test_python_binding_rejects_bad_tensors():
     q = torch.zeros(2, 3, 1, 8)
     with pytest.raises(ValueError):
         ea.evoattn_fwd(q, q, q)          # CPU tensors are rejected before any library call
+
+
+def proj(**kw):
+    lib = _lib.load()
+    args = dict(a=8, b=8, c=128, heads=4, head_dim=32, dtype=1, bt=0, eps=1e-5, x=A, gamma=A, beta=A,
+                w_qkv=A, w_bias=A, q=A, k=A, v=A, bias=A, mean=A, rstd=A)
+    args.update(kw)
+    return lib.evoattn_ln_proj_fwd(args["a"], args["b"], args["c"], args["heads"], args["head_dim"], args["dtype"],
+                                   args["bt"], args["eps"], args["x"], args["gamma"], args["beta"], args["w_qkv"],
+                                   args["w_bias"], args["q"], args["k"], args["v"], args["bias"], args["mean"],
+                                   args["rstd"], None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(a=0), INVALID, "sizes"),
+    (dict(c=-1), INVALID, "sizes"),
+    (dict(dtype=3), INVALID, "dtype"),
+    (dict(bt=2), INVALID, "bias_transpose"),
+    (dict(eps=-1.0), INVALID, "eps"),
+    (dict(eps=float("nan")), INVALID, "eps"),
+    (dict(w_qkv=None, w_bias=None, q=None, k=None, v=None, bias=None), INVALID, "nothing to project"),
+    (dict(head_dim=24), UNSUPPORTED, "head_dim"),
+    (dict(c=12), UNSUPPORTED, "channels"),
+    (dict(c=4096), UNSUPPORTED, "channels"),
+    (dict(c=100), UNSUPPORTED, "channels"),
+    (dict(a=8, b=9), INVALID, "square"),
+    (dict(a=1 << 16, b=1 << 16, w_bias=None, bias=None), UNSUPPORTED, "too large"),
+    (dict(x=None), INVALID, "x must not be NULL"),
+    (dict(gamma=None), INVALID, "gamma must not be NULL"),
+    (dict(beta=A + 2), INVALID, "aligned"),
+    (dict(q=None), INVALID, "q must not be NULL"),
+    (dict(v=A + 8), INVALID, "aligned"),
+    (dict(w_qkv=None), INVALID, "must be NULL when w_qkv is NULL"),
+    (dict(bias=None), INVALID, "bias must not be NULL"),
+    (dict(w_bias=None), INVALID, "bias must be NULL"),
+    (dict(mean=None), INVALID, "both"),
+    (dict(rstd=A + 2), INVALID, "aligned"),
+])
+def test_ln_proj_fwd_validation(kw, code, needle):
+    assert proj(**kw) == code
+    assert needle in detail()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful where no GPU is present")
+def test_ln_proj_valid_call_without_device_reports_device_error():
+    assert proj() == DEVICE
+    assert proj(w_qkv=None, q=None, k=None, v=None, a=5, b=5, mean=None, rstd=None) == DEVICE
+    assert proj(w_bias=None, bias=None, a=7, b=3) == DEVICE
+
+
+def test_ln_proj_binding_rejects_bad_tensors():
+    import af3_attention_amd as ea
+    x = torch.zeros(2, 2, 16)
+    with pytest.raises(ValueError):
+        ea.ln_proj_fwd(x, torch.ones(16), torch.zeros(16), heads=1, head_dim=8)

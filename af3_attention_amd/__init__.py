@@ -12,4 +12,5 @@ from .evoattn import (  # noqa: F401
     evoattn_fwd_workspace_bytes,
 )
 from ._lib import EvoAttnError, LIB_PATH  # noqa: F401
-from .evofusion import ln_proj_fwd  # noqa: F401,E402
+from .evofusion import (  # noqa: F401,E402
+    LNProjFunction, ln_proj, ln_proj_bwd, ln_proj_bwd_workspace_bytes, ln_proj_fwd)

@@ -17,6 +17,8 @@ EXPORTS = (
     "evoattn_timing_enable",
     "evoattn_timing_collect",
     "evoattn_ln_proj_fwd",
+    "evoattn_ln_proj_bwd_workspace_bytes",
+    "evoattn_ln_proj_bwd",
 )
 
 _lib = None
@@ -53,6 +55,11 @@ def load():
     lib.evoattn_ln_proj_fwd.argtypes = [i64, i64, i64, i64, i64, c_int, c_int, ctypes.c_float,
                                         vp, fp, fp, vp, vp, vp, vp, vp, vp, fp, fp, vp]
     lib.evoattn_ln_proj_fwd.restype = c_int
+    lib.evoattn_ln_proj_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, c_int, c_int, c_int]
+    lib.evoattn_ln_proj_bwd_workspace_bytes.restype = sz
+    lib.evoattn_ln_proj_bwd.argtypes = [i64, i64, i64, i64, i64, c_int, c_int, vp, fp, fp, vp, vp, fp, fp,
+                                        vp, vp, vp, fp, vp, fp, fp, fp, fp, vp, sz, vp]
+    lib.evoattn_ln_proj_bwd.restype = c_int
     lib.evoattn_timing_enable.argtypes = [c_int]
     lib.evoattn_timing_enable.restype = None
     lib.evoattn_timing_collect.argtypes = [c_int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),

@@ -271,4 +271,60 @@ evoattn_status_t evoattn_ln_proj_fwd(int64_t a, int64_t b, int64_t channels, int
   return EVOATTN_OK;
 }
 
+size_t evoattn_ln_proj_bwd_workspace_bytes(int64_t a, int64_t b, int64_t channels, int64_t heads, int64_t head_dim,
+                                           int dtype, int with_qkv, int with_bias) {
+  evo::ProjProblem p;
+  if (check_proj(a, b, channels, heads, head_dim, dtype, 0, 0.f, with_qkv != 0, with_bias != 0, &p) != EVOATTN_OK)
+    return 0;
+  return round_up(evo::ln_proj_bwd_workspace_bytes(p));
+}
+
+evoattn_status_t evoattn_ln_proj_bwd(int64_t a, int64_t b, int64_t channels, int64_t heads, int64_t head_dim,
+                                     int dtype, int bias_transpose, const void* x, const float* gamma,
+                                     const float* beta, const void* w_qkv, const void* w_bias, const float* mean,
+                                     const float* rstd, const void* dq, const void* dk, const void* dv,
+                                     const float* dbias, void* dx, float* dgamma, float* dbeta, float* dw_qkv,
+                                     float* dw_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  evo::ProjProblem p;
+  evoattn_status_t st = check_proj(a, b, channels, heads, head_dim, dtype, bias_transpose, 0.f, w_qkv != nullptr,
+                                   w_bias != nullptr, &p);
+  if (st != EVOATTN_OK) return st;
+  REQUIRE_PTR(x, 16);
+  REQUIRE_PTR(gamma, 4);
+  REQUIRE_PTR(beta, 4);
+  REQUIRE_PTR(mean, 4);
+  REQUIRE_PTR(rstd, 4);
+  REQUIRE_PTR(dx, 16);
+  REQUIRE_PTR(dgamma, 4);
+  REQUIRE_PTR(dbeta, 4);
+  if (w_qkv) {
+    REQUIRE_PTR(w_qkv, 16);
+    REQUIRE_PTR(dq, 16);
+    REQUIRE_PTR(dk, 16);
+    REQUIRE_PTR(dv, 16);
+    REQUIRE_PTR(dw_qkv, 4);
+  } else if (dq || dk || dv || dw_qkv) {
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "dq, dk, dv and dw_qkv must be NULL when w_qkv is NULL");
+  }
+  if (w_bias) {
+    REQUIRE_PTR(w_bias, 16);
+    REQUIRE_PTR(dbias, 4);
+    REQUIRE_PTR(dw_bias, 4);
+  } else if (dbias || dw_bias) {
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "dbias and dw_bias must be NULL when w_bias is NULL");
+  }
+  const size_t need = round_up(evo::ln_proj_bwd_workspace_bytes(p));
+  if (!workspace || workspace_bytes < need)
+    return fail(EVOATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu at %p", need, workspace_bytes, workspace);
+  if (!aligned(workspace, 256)) return fail(EVOATTN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if ((st = check_device()) != EVOATTN_OK) return st;
+
+  evo::ProjBwdArgs args{x, gamma, beta, w_qkv, w_bias, mean, rstd, dq, dk, dv, dbias, dx, dgamma, dbeta, dw_qkv, dw_bias};
+  hipError_t e = evo::launch_ln_proj_bwd(p, args, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(EVOATTN_ERR_DEVICE, "layer norm + projection backward launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return EVOATTN_OK;
+}
+
 }  // extern "C"

@@ -116,6 +116,29 @@ struct ProjFwdArgs {
 
 hipError_t launch_ln_proj_fwd(const ProjProblem& p, const ProjFwdArgs& a, hipStream_t s);
 
+struct ProjBwdArgs {
+  const void* x;
+  const float* gamma;
+  const float* beta;
+  const void* w_qkv;   // [n_qkv][C] or nullptr
+  const void* w_bias;  // [H][C] or nullptr
+  const float* mean;   // [T]
+  const float* rstd;   // [T]
+  const void* dq;      // upstream gradients of q, k, v [T][H*D] (with w_qkv)
+  const void* dk;
+  const void* dv;
+  const float* dbias;  // upstream gradient of the bias [H][A][B] fp32 (with w_bias)
+  void* dx;            // [T][C]
+  float* dgamma;       // [C]
+  float* dbeta;        // [C]
+  float* dw_qkv;       // [n_qkv][C] (with w_qkv)
+  float* dw_bias;      // [H][C] (with w_bias)
+};
+
+// Workspace of the backward in bytes, and its launch.
+size_t ln_proj_bwd_workspace_bytes(const ProjProblem& p);
+hipError_t launch_ln_proj_bwd(const ProjProblem& p, const ProjBwdArgs& a, void* ws, hipStream_t s);
+
 // bf16 storage conversions (round to nearest even; NaN stays NaN).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

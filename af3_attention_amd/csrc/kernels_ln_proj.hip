@@ -23,40 +23,16 @@
 
 #include "evoattn_internal.h"
 #include "mfma_common.h"
+#include "proj_common.h"
 
 namespace evo {
 namespace {
 
 using namespace mfma;
+using namespace proj;
 
 constexpr int kProjWaves = 8;
 constexpr int kProjThreads = 64 * kProjWaves;
-
-// Token of slot i (0..31) of 32-token tile `tile`, or -1 past the end.  Row
-// tiles take 32 consecutive tokens; column tiles take 32 consecutive a at one b,
-// so a transposed bias is written in 64-byte runs.
-__device__ __forceinline__ int64_t tile_token(const ProjProblem& p, int tile, int i) {
-  if (!p.col_tiles) {
-    const int64_t t = static_cast<int64_t>(tile) * 32 + i;
-    return t < p.T ? t : -1;
-  }
-  const int nab = (p.A + 31) >> 5;
-  const int b = tile / nab;
-  const int a = (tile - b * nab) * 32 + i;
-  return a < p.A ? static_cast<int64_t>(a) * p.B + b : -1;
-}
-
-__device__ __forceinline__ int64_t bias_offset(const ProjProblem& p, int hb, int64_t tok) {
-  int64_t pos = tok;
-  if (p.bias_transpose) {
-    const int64_t a = tok / p.B;
-    pos = (tok - a * p.B) * p.A + a;
-  }
-  return static_cast<int64_t>(hb) * p.T + pos;
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
 

@@ -46,3 +46,83 @@ def ln_proj_fwd(x, gamma, beta, w_qkv=None, w_bias=None, *, heads: int, head_dim
                                  _ptr(out["mean"]), _ptr(out["rstd"]), _stream(dev))
     _lib.check(st, "evoattn_ln_proj_fwd")
     return out
+
+
+def ln_proj_bwd_workspace_bytes(a, b, channels, heads, head_dim, dtype=torch.bfloat16, with_qkv=True,
+                                with_bias=True) -> int:
+    return int(_lib.load().evoattn_ln_proj_bwd_workspace_bytes(a, b, channels, heads, head_dim, _DTYPES[dtype],
+                                                                int(bool(with_qkv)), int(bool(with_bias))))
+
+
+def ln_proj_bwd(x, gamma, beta, w_qkv, w_bias, mean, rstd, dq=None, dk=None, dv=None, dbias=None, *,
+                heads: int, head_dim: int, bias_transpose: bool = False, workspace=None):
+    """Gradients of sum(q*dq) + sum(k*dk) + sum(v*dv) + sum(bias*dbias) through ln_proj_fwd.
+
+    dbias is fp32 [H, A, B] (as evoattn_bwd returns it).  Returns dict dx (x's dtype),
+    dgamma, dbeta (fp32 [C]), dw_qkv (fp32 [3Hd, C] or None), dw_bias (fp32 [H, C] or None)."""
+    lib = _lib.load()
+    A, B, C = x.shape
+    dev = x.device
+    hd = heads * head_dim
+    _check(x, "x", x.shape, x.dtype, dev)
+    _check(gamma, "gamma", (C,), torch.float32, dev)
+    _check(beta, "beta", (C,), torch.float32, dev)
+    _check(w_qkv, "w_qkv", (3 * hd, C), x.dtype, dev, optional=True)
+    _check(w_bias, "w_bias", (heads, C), x.dtype, dev, optional=True)
+    _check(mean, "mean", (A * B,), torch.float32, dev)
+    _check(rstd, "rstd", (A * B,), torch.float32, dev)
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, n, (A, B, heads, head_dim), x.dtype, dev, optional=w_qkv is None)
+    _check(dbias, "dbias", (heads, A, B), torch.float32, dev, optional=w_bias is None)
+    out = {"dx": torch.empty_like(x),
+           "dgamma": torch.empty(C, dtype=torch.float32, device=dev),
+           "dbeta": torch.empty(C, dtype=torch.float32, device=dev),
+           "dw_qkv": None if w_qkv is None else torch.empty((3 * hd, C), dtype=torch.float32, device=dev),
+           "dw_bias": None if w_bias is None else torch.empty((heads, C), dtype=torch.float32, device=dev)}
+    ws_bytes = ln_proj_bwd_workspace_bytes(A, B, C, heads, head_dim, x.dtype, w_qkv is not None, w_bias is not None)
+    ws = workspace
+    if ws is None or ws.numel() < ws_bytes:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.evoattn_ln_proj_bwd(A, B, C, heads, head_dim, _DTYPES[x.dtype], int(bool(bias_transpose)),
+                                 _ptr(x), _ptr(gamma), _ptr(beta), _ptr(w_qkv), _ptr(w_bias), _ptr(mean),
+                                 _ptr(rstd), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(out["dx"]),
+                                 _ptr(out["dgamma"]), _ptr(out["dbeta"]), _ptr(out["dw_qkv"]),
+                                 _ptr(out["dw_bias"]), _ptr(ws), ws_bytes, _stream(dev))
+    _lib.check(st, "evoattn_ln_proj_bwd")
+    return out
+
+
+class LNProjFunction(torch.autograd.Function):
+    """Differentiable fused layer norm + projections; outputs (q, k, v, bias), None where absent."""
+
+    @staticmethod
+    def forward(ctx, x, gamma, beta, w_qkv, w_bias, heads, head_dim, bias_transpose, eps):
+        x = x.contiguous()
+        out = ln_proj_fwd(x, gamma, beta, w_qkv, w_bias, heads=heads, head_dim=head_dim,
+                          bias_transpose=bias_transpose, eps=eps)
+        ctx.save_for_backward(x, gamma, beta, w_qkv, w_bias, out["mean"], out["rstd"])
+        ctx.cfg = (heads, head_dim, bias_transpose)
+        return out["q"], out["k"], out["v"], out["bias"]
+
+    @staticmethod
+    def backward(ctx, dq, dk, dv, dbias):
+        x, gamma, beta, w_qkv, w_bias, mean, rstd = ctx.saved_tensors
+        heads, head_dim, bt = ctx.cfg
+        shape = (x.shape[0], x.shape[1], heads, head_dim)
+        if w_qkv is not None:
+            dq, dk, dv = (torch.zeros(shape, dtype=x.dtype, device=x.device) if g is None else g.contiguous()
+                          for g in (dq, dk, dv))
+        if w_bias is not None:
+            dbias = (torch.zeros((heads, x.shape[0], x.shape[1]), dtype=torch.float32, device=x.device)
+                     if dbias is None else dbias.float().contiguous())
+        g = ln_proj_bwd(x, gamma, beta, w_qkv, w_bias, mean, rstd, dq, dk, dv, dbias, heads=heads,
+                        head_dim=head_dim, bias_transpose=bt)
+        dwq = None if g["dw_qkv"] is None else g["dw_qkv"].to(w_qkv.dtype)
+        dwb = None if g["dw_bias"] is None else g["dw_bias"].to(w_bias.dtype)
+        return g["dx"], g["dgamma"], g["dbeta"], dwq, dwb, None, None, None, None
+
+
+def ln_proj(x, gamma, beta, w_qkv=None, w_bias=None, *, heads: int, head_dim: int, bias_transpose: bool = False,
+            eps: float = 1e-5):
+    """Differentiable layer norm + projections: returns (q, k, v, bias), None where absent."""
+    return LNProjFunction.apply(x, gamma, beta, w_qkv, w_bias, heads, head_dim, bool(bias_transpose), float(eps))

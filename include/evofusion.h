@@ -38,7 +38,9 @@
  * ---------------------------------------------------------------- ownership
  * Every pointer except `stream` is a device pointer owned by the caller.  The
  * library allocates nothing; outputs are overwritten; inputs and outputs must
- * not overlap.  Work is enqueued on `stream` (NULL = default stream).
+ * not overlap.  The backward's scratch space is passed in as `workspace` of at
+ * least evoattn_ln_proj_bwd_workspace_bytes() (256-byte aligned; contents on
+ * entry do not matter).  Work is enqueued on `stream` (NULL = default stream).
  *
  * ---------------------------------------------------------------- errors
  * Arguments are validated before anything is enqueued; the return value is an
@@ -68,6 +70,32 @@ evoattn_status_t evoattn_ln_proj_fwd(int64_t a, int64_t b, int64_t channels, int
                                      const void* w_qkv, const void* w_bias,
                                      void* q, void* k, void* v, void* bias,
                                      float* mean, float* rstd, void* stream);
+
+/* Bytes of workspace evoattn_ln_proj_bwd needs (fixed-order partial sums over
+ * at most 64 token ranges; O((3*H*d + H) * C)).  with_qkv / with_bias say which
+ * weights the call has.  Returns 0 and records an error detail if the problem
+ * is invalid. */
+size_t evoattn_ln_proj_bwd_workspace_bytes(int64_t a, int64_t b, int64_t channels, int64_t heads,
+                                           int64_t head_dim, int dtype, int with_qkv, int with_bias);
+
+/* Backward of L = sum q*dq + sum k*dk + sum v*dv + sum bias*dbias through the
+ * forward above.  Inputs: the forward's x, gamma, beta, weights, its mean and
+ * rstd (required), and the upstream gradients dq, dk, dv (dtype, layout of q;
+ * exactly when w_qkv is given) and dbias (fp32 [H, A, B] in the kernel frame
+ * as evoattn_bwd writes it; exactly when w_bias is given).  Outputs: dx (dtype,
+ * layout of x), dgamma, dbeta (fp32 [C]), dw_qkv (fp32 [3*H*d, C], with w_qkv)
+ * and dw_bias (fp32 [H, C], with w_bias).  The sums over tokens run in a fixed
+ * order: results are bit-identical across calls with the same inputs.  In bf16
+ * mode dbias and xhat are rounded to bf16 as matrix-core operands; every sum is
+ * fp32. */
+evoattn_status_t evoattn_ln_proj_bwd(int64_t a, int64_t b, int64_t channels, int64_t heads,
+                                     int64_t head_dim, int dtype, int bias_transpose,
+                                     const void* x, const float* gamma, const float* beta,
+                                     const void* w_qkv, const void* w_bias,
+                                     const float* mean, const float* rstd,
+                                     const void* dq, const void* dk, const void* dv, const float* dbias,
+                                     void* dx, float* dgamma, float* dbeta, float* dw_qkv, float* dw_bias,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -207,3 +207,55 @@ def test_ln_proj_binding_rejects_bad_tensors():
     x = torch.zeros(2, 2, 16)
     with pytest.raises(ValueError):
         ea.ln_proj_fwd(x, torch.ones(16), torch.zeros(16), heads=1, head_dim=8)
+
+
+def proj_bwd(**kw):
+    lib = _lib.load()
+    args = dict(a=8, b=8, c=128, heads=4, head_dim=32, dtype=1, bt=0, x=A, gamma=A, beta=A, w_qkv=A, w_bias=A,
+                mean=A, rstd=A, dq=A, dk=A, dv=A, dbias=A, dx=A, dgamma=A, dbeta=A, dw_qkv=A, dw_bias=A, ws=A,
+                ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.evoattn_ln_proj_bwd(*(args[k] for k in (
+        "a", "b", "c", "heads", "head_dim", "dtype", "bt", "x", "gamma", "beta", "w_qkv", "w_bias", "mean", "rstd",
+        "dq", "dk", "dv", "dbias", "dx", "dgamma", "dbeta", "dw_qkv", "dw_bias", "ws", "ws_bytes")), None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(b=-1), INVALID, "sizes"),
+    (dict(head_dim=12), UNSUPPORTED, "head_dim"),
+    (dict(a=8, b=7), INVALID, "square"),
+    (dict(mean=None), INVALID, "mean must not be NULL"),
+    (dict(rstd=None), INVALID, "rstd must not be NULL"),
+    (dict(dx=None), INVALID, "dx must not be NULL"),
+    (dict(dgamma=None), INVALID, "dgamma must not be NULL"),
+    (dict(dbeta=A + 1), INVALID, "aligned"),
+    (dict(dq=None), INVALID, "dq must not be NULL"),
+    (dict(dw_qkv=None), INVALID, "dw_qkv must not be NULL"),
+    (dict(dbias=None), INVALID, "dbias must not be NULL"),
+    (dict(dw_bias=None), INVALID, "dw_bias must not be NULL"),
+    (dict(w_qkv=None), INVALID, "must be NULL when w_qkv is NULL"),
+    (dict(w_bias=None), INVALID, "must be NULL when w_bias is NULL"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(ws_bytes=16), WORKSPACE, "workspace"),
+    (dict(ws=A + 64), INVALID, "256-byte"),
+])
+def test_ln_proj_bwd_validation(kw, code, needle):
+    assert proj_bwd(**kw) == code
+    assert needle in detail()
+
+
+def test_ln_proj_bwd_workspace_query():
+    lib = _lib.load()
+    n = lib.evoattn_ln_proj_bwd_workspace_bytes(384, 384, 128, 4, 32, 1, 1, 1)
+    assert n % 256 == 0
+    # partial sums over at most 64 token ranges of a (3*H*d + H, padded to 32) x C array, plus two
+    # (3*H*d + H) x C product arrays: independent of N beyond the range count
+    assert n <= 64 * 416 * 128 * 4 + 64 * 416 * 4 + 2 * 388 * 128 * 4 + 4 * 256
+    assert n == lib.evoattn_ln_proj_bwd_workspace_bytes(1536, 1536, 128, 4, 32, 1, 1, 1)
+    assert lib.evoattn_ln_proj_bwd_workspace_bytes(8, 9, 128, 4, 32, 1, 1, 1) == 0   # bias needs a == b
+    assert lib.evoattn_ln_proj_bwd_workspace_bytes(8, 8, 128, 4, 32, 1, 0, 0) == 0   # nothing to project
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful where no GPU is present")
+def test_ln_proj_bwd_valid_call_without_device_reports_device_error():
+    assert proj_bwd() == DEVICE

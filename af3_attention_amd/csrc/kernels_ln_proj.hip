@@ -23,6 +23,7 @@
 
 #include "evoattn_internal.h"
 #include "mfma_common.h"
+#include "pipe_common.h"
 #include "proj_common.h"
 
 namespace evo {
@@ -98,6 +99,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void ln_proj_fwd_mfma(ProjProblem 
     }
   }
   __syncthreads();
+  // Wait for the first tile here, outside the loop: the loop then starts in the
+  // same state on every trip, and the compiler's wait before the first use of x
+  // does not also wait for the next tile's prefetch.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) pipe::retire(xr[ks]);
 
   const int hd = p.H * p.D;
   uint16_t* const qg = static_cast<uint16_t*>(a.q);
@@ -129,6 +135,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void ln_proj_fwd_mfma(ProjProblem 
     const float rstd = rsqrtf(fmaf(pair_sum(ss), inv_c, p.eps));
 
     const int64_t tok = tile_token(p, tile, li);
+    const int64_t bpos = (biasg && tok >= 0) ? bias_pos(p, tok) : 0;
     if (half == 0 && tok >= 0 && a.mean) {
       a.mean[tok] = mean;
       a.rstd[tok] = rstd;
@@ -182,10 +189,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void ln_proj_fwd_mfma(ProjProblem 
         } else if (o8 < p.n_out) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const int o = o8 + j;
-            if (o >= p.n_qkv && o < p.n_out) {
+            const int hb = o8 + j - p.n_qkv;
+            if (hb >= 0 && hb < p.H) {
               const uint32_t w = out[j >> 1];
-              biasg[bias_offset(p, o - p.n_qkv, tok)] = static_cast<uint16_t>((j & 1) ? (w >> 16) : (w & 0xffffu));
+              biasg[static_cast<int64_t>(hb) * p.T + bpos] = static_cast<uint16_t>((j & 1) ? (w >> 16) : (w & 0xffffu));
             }
           }
         }

@@ -15,7 +15,7 @@
 //      swapped (W^T resident in LDS, G streamed from HBM as the MFMA operand,
 //      the layer-norm backward on registers; each token's channels sit on two lanes).
 //   2. Partial M and s over fixed token ranges: one workgroup per (group of four
-//      32-output tiles, token range); G and xhat are staged in LDS per 64 tokens
+//      32-output tiles, token range); G and xhat are staged in LDS per 128 tokens
 //      and read back transposed so that tokens are the contraction index.  The
 //      groups of one range run on one XCD, so x is fetched from HBM once.
 //   3. Finalize: partials summed in increasing range order, dW, the products
@@ -43,7 +43,7 @@ using pipe::xcd_logical_block;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 64;       // tokens per staged chunk of the partial-sum kernel
+constexpr int kChunk = 128;      // tokens per staged chunk of the partial-sum kernel
 constexpr int kGroupOut = 128;   // outputs per group (four 32-output tiles)
 constexpr int kMaxRanges = 64;   // token ranges of the partial sums
 constexpr size_t kMaxLds = 160 * 1024;
@@ -51,7 +51,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 // Rows of the partial-M array: outputs padded to whole 32-output tiles.
 __host__ __device__ __forceinline__ int padded_outputs(const ProjProblem& p) { return (p.n_out + 31) / 32 * 32; }
 
-// Number of token ranges and 64-token chunks per range.
+// Number of token ranges and kChunk-token chunks per range.
 void range_split(const ProjProblem& p, int* ranges, int* range_chunks) {
   const int64_t chunks = (p.T + kChunk - 1) / kChunk;
   int64_t r = chunks < kMaxRanges ? chunks : kMaxRanges;
@@ -61,35 +61,67 @@ void range_split(const ProjProblem& p, int* ranges, int* range_chunks) {
   *range_chunks = static_cast<int>(per);
 }
 
-// 8 upstream gradients G[tok][o0 .. o0+7] as packed bf16 (o0 a multiple of 8):
-// a 16-byte load of a dq/dk/dv row, or the bias heads gathered from dbias.
-__device__ __forceinline__ u32x4 g_piece(const ProjProblem& p, const ProjBwdArgs& a, int64_t tok, int o0) {
-  if (o0 >= p.n_out) return u32x4{0, 0, 0, 0};
+// Width of the token-order pair-bias gradient buffer: H rounded up to 16, so
+// that every 16-output k-step over it is one full load per lane.
+__host__ __device__ __forceinline__ int bias_width(const ProjProblem& p) {
+  return p.n_out > p.n_qkv ? (p.H + 15) / 16 * 16 : 0;
+}
+
+// Source of the 8 upstream gradients G[tok][o0 .. o0+7] (o0 a multiple of 8) as
+// one 16-byte bf16 load: a dq/dk/dv row, or the token-order bias buffer gb
+// [T][bias_width] (written by bias_grad_tokens), or nothing (zero).
+struct GSource {
+  const uint16_t* base;  // element (tok, o0) at base + tok * pitch
+  int pitch;
+};
+__device__ __forceinline__ GSource g_source(const ProjProblem& p, const ProjBwdArgs& a, const uint16_t* gb,
+                                            int o0) {
   const int hd = p.H * p.D;
-  if (o0 + 8 <= p.n_qkv) {
+  if (o0 < p.n_qkv) {
     const int which = o0 / hd;
-    const int col = o0 - which * hd;
     const uint16_t* src = static_cast<const uint16_t*>(which == 0 ? a.dq : (which == 1 ? a.dk : a.dv));
-    return *reinterpret_cast<const u32x4*>(src + tok * hd + col);
+    return GSource{src + (o0 - which * hd), hd};
   }
-  float v[8];
+  const int hb = bias_width(p);
+  if (o0 < p.n_qkv + hb) return GSource{gb + (o0 - p.n_qkv), hb};
+  return GSource{nullptr, 0};
+}
+__device__ __forceinline__ u32x4 g_load(const GSource& g, int64_t tok) {
+  return g.base ? *reinterpret_cast<const u32x4*>(g.base + tok * g.pitch) : u32x4{0, 0, 0, 0};
+}
+
+// The pair-bias gradient (fp32, [H][A][B] in the attention's frame) in token
+// order as bf16, zero-padded to bias_width: one thread per token.
+__global__ __launch_bounds__(256) void bias_grad_tokens(ProjProblem p, ProjBwdArgs a, uint16_t* gb) {
+  const int64_t tok = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (tok >= p.T) return;
+  const int hb = bias_width(p);
+  const float* src = a.dbias + bias_pos(p, tok);
+  for (int h0 = 0; h0 < hb; h0 += 8) {
+    float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int o = o0 + e;
-    v[e] = (o >= p.n_qkv && o < p.n_out) ? a.dbias[bias_offset(p, o - p.n_qkv, tok)] : 0.f;
+    for (int e = 0; e < 8; ++e) v[e] = h0 + e < p.H ? src[static_cast<int64_t>(h0 + e) * p.T] : 0.f;
+    *reinterpret_cast<u32x4*>(gb + tok * hb + h0) =
+        u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
   }
-  return u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
 }
 
 // ---------------------------------------------------------------- 1. dx (MFMA)
 
+// k-steps per dx tile the MFMA kernel holds in registers.
+template <int KS>
+constexpr int dx_max_ksteps() { return KS >= 8 ? 25 : 32; }
+
 // LDS: gamma[C] fp32, then W^T: row c holds W[0..ko)[c] (bf16; zero past n_out)
 // with a pitch of 2*ko + 16 bytes.
-template <int KS>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBwdArgs a, int ko) {
+// HDK = H*D/16 (H*D in {32, 64, 128}, q/k/v present, at most 16 bias heads):
+// k-step j < 3 HDK reads q/k/v row `j / HDK` at a compile-time offset from one
+// per-tile row pointer, and k-step 3 HDK (when there is a bias) the bias buffer.
+template <int KS, int HDK>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBwdArgs a, const uint16_t* gb, int ko) {
   constexpr int C = 16 * KS;
   constexpr int CT = KS / 2;  // 32-channel tiles
-  constexpr int NB = KS >= 8 ? 4 : 8;  // k-steps (16 outputs each) per batch of G loads
+  constexpr int NB = dx_max_ksteps<KS>();  // k-steps (16 outputs each) held in registers
   extern __shared__ __align__(16) char lds[];
   float* s_gamma = reinterpret_cast<float*>(lds);
   char* s_wt = lds + 4 * C;
@@ -127,37 +159,67 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBw
 
   const uint16_t* xg = static_cast<const uint16_t*>(a.x);
   uint16_t* dxg = static_cast<uint16_t*>(a.dx);
-  const int nks = ko / 16;
-  const int nks_q = p.n_qkv / 16;  // k-steps made only of q/k/v outputs
-  const int nbatch = (nks_q + NB - 1) / NB;
-  const int hd = p.H * p.D;
+  const int nks = ko / 16;  // <= NB (checked by the launcher)
   constexpr float inv_c = 1.0f / C;
   const int stride = gridDim.x * kWaves;
+  const int hd = p.H * p.D;
+  const int hb = bias_width(p);
+  const uint16_t* const dqg = static_cast<const uint16_t*>(a.dq);
+  const uint16_t* const dkg = static_cast<const uint16_t*>(a.dk);
+  const uint16_t* const dvg = static_cast<const uint16_t*>(a.dv);
 
   for (int tile = blockIdx.x * kWaves + wave; tile < p.tiles; tile += stride) {
     const int64_t tok = tile_token(p, tile, li);
     const bool valid = tok >= 0;
     const int64_t tk = valid ? tok : 0;
 
-    // Full q/k/v k-steps: 16-byte loads of dq/dk/dv rows, in batches of NB.
-    auto load_batch = [&](int b, u32x4* dst) {
+    // dy^T tile per 32 channels: D[c][t] = sum_o W^T[c][o] G[t][o].
+    f32x16 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x16{};
+    // W^T operands of k-step ks for every channel tile.
+    auto read_w = [&](int ks, u32x4* w) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        w[ct] = *reinterpret_cast<const u32x4*>(s_wt + (32 * ct + li) * pw + (16 * ks + 8 * half) * 2);
+    };
+    // Products of k-steps 0 .. n-1: each step's W^T reads are issued one step ahead,
+    // and a scheduling barrier keeps the compiler from hoisting more of them.
+    auto run_steps = [&](int n, const u32x4* g) {
+      u32x4 wc[CT], wn[CT];
+      read_w(0, wc);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int ks = NB * b + j;
-        u32x4 v = {0, 0, 0, 0};
-        if (valid && ks < nks_q) {
-          const int o0 = 16 * ks + 8 * half;
-          const int which = o0 / hd;
-          const uint16_t* src = static_cast<const uint16_t*>(which == 0 ? a.dq : (which == 1 ? a.dk : a.dv));
-          v = *reinterpret_cast<const u32x4*>(src + tk * hd + (o0 - which * hd));
+        if (j < n) {
+          if (j + 1 < n) read_w(j + 1, wn);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc[ct] = mma(wc[ct], g[j], acc[ct]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) wc[ct] = wn[ct];
         }
-        dst[j] = v;
       }
     };
-    u32x4 gcur[NB], gnext[NB];
-    load_batch(0, gcur);
+    // Every k-step's upstream gradients are one 16-byte load; a batch (up to NB
+    // k-steps, normally the whole tile) is issued before its first product.
+    {
+      constexpr int NQ = 3 * HDK;
+      static_assert(HDK > 0 && NQ + 1 <= NB, "q/k/v and bias k-steps must fit the register batch");
+      u32x4 gq[NB];
+      const int64_t oq = tk * (16 * HDK) + 8 * half;
+      const uint16_t* rows[3] = {dqg + oq, dkg + oq, dvg + oq};
+#pragma unroll
+      for (int w3 = 0; w3 < 3; ++w3)
+#pragma unroll
+        for (int c = 0; c < HDK; ++c)
+          gq[w3 * HDK + c] = valid ? *reinterpret_cast<const u32x4*>(rows[w3] + 16 * c) : u32x4{0, 0, 0, 0};
+      const bool has_bias = hb > 0;
+      gq[NQ] = (valid && has_bias) ? *reinterpret_cast<const u32x4*>(gb + tk * hb + 8 * half) : u32x4{0, 0, 0, 0};
+      run_steps(has_bias ? NQ + 1 : NQ, gq);
+    }
 
-    // x at the accumulator's channels: 32 ct + 8 g + 4 half + 0..3.
+    // x at the accumulator's channels (32 ct + 8 g + 4 half + 0..3), requested after
+    // the products so that the upstream gradients alone occupy the load registers.
     u32x2 xr[CT][4];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -167,28 +229,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBw
                           : u32x2{0, 0};
     const float mean = valid ? a.mean[tk] : 0.f;
     const float rstd = valid ? a.rstd[tk] : 0.f;
-
-    // dy^T tile per 32 channels: D[c][t] = sum_o W^T[c][o] G[t][o].
-    f32x16 acc[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x16{};
-    auto step = [&](int ks, const u32x4& g) {
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(s_wt + (32 * ct + li) * pw + (16 * ks + 8 * half) * 2);
-        acc[ct] = mma(w, g, acc[ct]);
-      }
-    };
-    for (int b = 0; b < nbatch; ++b) {
-      if (b + 1 < nbatch) load_batch(b + 1, gnext);
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        if (NB * b + j < nks_q) step(NB * b + j, gcur[j]);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) gcur[j] = gnext[j];
-    }
-    // Remaining k-steps: the pair-bias heads (and a last half q/k/v step).
-    for (int ks = nks_q; ks < nks; ++ks) step(ks, valid ? g_piece(p, a, tk, 16 * ks + 8 * half) : u32x4{0, 0, 0, 0});
 
     // Layer-norm backward on the token's channels (this lane's half, then the partner's).
     float s1 = 0.f, s2 = 0.f;
@@ -240,14 +280,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBw
 
 // ---------------------------------------------------------------- 2. partial M, s (MFMA)
 
-// LDS per stage: G [64 tokens][128 outputs] bf16 (pitch 288 B), then
-// xhat [64 tokens][C] bf16 (pitch 2C + 32 B).  Two stages.
+// LDS per stage: G [128 tokens][128 outputs] bf16 (pitch 288 B), then
+// xhat [128 tokens][C] bf16 (pitch 2C + 32 B).  Two stages.
 template <int KS>
 constexpr int mpart_stage_bytes() { return kChunk * ((2 * kGroupOut + 32) + (32 * KS + 32)); }
 
 template <int KS>
-__global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, ProjBwdArgs a, int n_groups, int ranges,
-                                                             int range_chunks, float* mpart, float* spart) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, ProjBwdArgs a, const uint16_t* gb,
+                                                             int n_groups, int ranges, int range_chunks, float* mpart,
+                                                             float* spart) {
   constexpr int C = 16 * KS;
   constexpr int CT = KS / 2;
   constexpr int PG = 2 * kGroupOut + 32;
@@ -278,18 +319,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
   const int nch = static_cast<int>((t_end - t_begin + kChunk - 1) / kChunk);
   const uint16_t* xg = static_cast<const uint16_t*>(a.x);
 
-  u32x4 gr[NGP];
-  u32x4 xr[NXP];
-  float xm[NXP], xs[NXP];
-  auto load = [&](int ch) {
+  // Every G piece of this thread has the same 8 outputs (kThreads is a multiple
+  // of GPL): one source for the whole kernel.
+  static_assert(kThreads % GPL == 0, "a thread's G pieces must share their outputs");
+  const GSource gsrc = g_source(p, a, gb, 32 * ot0 + 8 * (tid % GPL));
+  // One chunk's share of this thread in registers; two sets alternate so that a
+  // chunk's loads are issued two chunks before its LDS stage is written.
+  struct Regs {
+    u32x4 g[NGP];
+    u32x4 x[NXP];
+    float m[NXP], r[NXP];
+  };
+  auto load = [&](int ch, Regs& R) {
     const int64_t t0 = t_begin + static_cast<int64_t>(ch) * kChunk;
 #pragma unroll
     for (int i = 0; i < NGP; ++i) {
-      const int idx = tid + i * kThreads;
-      const int t = idx / GPL;
-      const int j = idx - t * GPL;
-      const int64_t tok = t0 + t;
-      gr[i] = tok < t_end ? g_piece(p, a, tok, 32 * ot0 + 8 * j) : u32x4{0, 0, 0, 0};
+      const int64_t tok = t0 + (tid + i * kThreads) / GPL;
+      R.g[i] = tok < t_end ? g_load(gsrc, tok) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < NXP; ++i) {
@@ -298,17 +344,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
       const int j = idx - t * XPL;
       const int64_t tok = t0 + t;
       if (idx < XP && tok < t_end) {
-        xr[i] = *reinterpret_cast<const u32x4*>(xg + tok * C + 8 * j);
-        xm[i] = a.mean[tok];
-        xs[i] = a.rstd[tok];
+        R.x[i] = *reinterpret_cast<const u32x4*>(xg + tok * C + 8 * j);
+        R.m[i] = a.mean[tok];
+        R.r[i] = a.rstd[tok];
       } else {
-        xr[i] = u32x4{0, 0, 0, 0};
-        xm[i] = 0.f;
-        xs[i] = 0.f;
+        R.x[i] = u32x4{0, 0, 0, 0};
+        R.m[i] = 0.f;
+        R.r[i] = 0.f;
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](const Regs& R, int buf) {
     char* sg = lds + buf * STAGE;
     char* sx = sg + kChunk * PG;
 #pragma unroll
@@ -316,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
       const int idx = tid + i * kThreads;
       const int t = idx / GPL;
       const int j = idx - t * GPL;
-      *reinterpret_cast<u32x4*>(sg + t * PG + 16 * j) = gr[i];
+      *reinterpret_cast<u32x4*>(sg + t * PG + 16 * j) = R.g[i];
     }
 #pragma unroll
     for (int i = 0; i < NXP; ++i) {
@@ -327,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          o[e] = pack_bf16((lo_bf16(xr[i][e]) - xm[i]) * xs[i], (hi_bf16(xr[i][e]) - xm[i]) * xs[i]);
+          o[e] = pack_bf16((lo_bf16(R.x[i][e]) - R.m[i]) * R.r[i], (hi_bf16(R.x[i][e]) - R.m[i]) * R.r[i]);
         *reinterpret_cast<u32x4*>(sx + t * PX + 16 * j) = o;
       }
     }
@@ -346,12 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   float s_acc = 0.f;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nch) load(ch + 1);
+  auto compute = [&](int buf) {
     const uint32_t sg = lds0 + buf * STAGE;
     const uint32_t sx = sg + kChunk * PG;
     if (tid < 32 * n_ot_g) {
@@ -359,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
 #pragma unroll 8
       for (int t = 0; t < kChunk; ++t) s_acc += bf16_to_f32(col[t * (PG / 2)]);
     }
-#pragma unroll
+#pragma unroll 2
     for (int kk = 0; kk < kChunk / 16; ++kk)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -369,7 +410,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
           acc[tt] = mma(tr(sg, PG, 32 * ot, kk), tr(sx, PX, 32 * ct, kk), acc[tt]);
         }
       }
-    if (ch + 1 < nch) store(buf ^ 1);
+  };
+
+  // Chunk ch is staged in LDS buffer ch % 2; register set A carries even chunks,
+  // B odd ones.
+  Regs RA, RB;
+  load(0, RA);
+  if (nch > 1) load(1, RB);
+  store(RA, 0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ch += 2) {
+    compute(0);
+    if (ch + 2 < nch) load(ch + 2, RA);
+    if (ch + 1 < nch) store(RB, 1);
+    __syncthreads();
+    if (ch + 1 >= nch) break;
+    compute(1);
+    if (ch + 3 < nch) load(ch + 3, RB);
+    if (ch + 2 < nch) store(RA, 0);
     __syncthreads();
   }
 
@@ -477,48 +535,81 @@ __global__ __launch_bounds__(kVecThreads) void bwd_mpart_vector(ProjProblem p, P
 
 // ---------------------------------------------------------------- 3. finalize
 
-// One workgroup per output row o: M and s from the partials (increasing range),
-// dW, and the per-(o, c) products whose sums over o are dgamma and dbeta.
+// One workgroup per output row o: M and s from the partials, dW, and the
+// per-(o, c) products whose sums over o are dgamma and dbeta.  Each of the four
+// wave slots sums every fourth range (in increasing order) for 64 channels; the
+// four partial sums are then added in slot order.
 template <typename T>
 __global__ __launch_bounds__(kVecThreads) void bwd_finalize_rows(ProjProblem p, ProjBwdArgs a, int ranges,
                                                                  const float* mpart, const float* spart,
                                                                  float* tgamma, float* tbeta) {
+  __shared__ float part[kVecThreads];
   const int o = blockIdx.x;
   const int po = padded_outputs(p);
+  const int slot = threadIdx.x >> 6;
+  const int cl = threadIdx.x & 63;
   float s = 0.f;
   for (int r = 0; r < ranges; ++r) s += spart[static_cast<int64_t>(r) * po + o];
-  for (int c = threadIdx.x; c < p.C; c += kVecThreads) {
+  for (int c0 = 0; c0 < p.C; c0 += 64) {
+    const int c = c0 + cl;
     float m = 0.f;
-    for (int r = 0; r < ranges; ++r) m += mpart[(static_cast<int64_t>(r) * po + o) * p.C + c];
-    const float dw = fmaf(m, a.gamma[c], s * a.beta[c]);
-    if (o < p.n_qkv)
-      a.dw_qkv[static_cast<int64_t>(o) * p.C + c] = dw;
-    else
-      a.dw_bias[static_cast<int64_t>(o - p.n_qkv) * p.C + c] = dw;
-    const float w = w_elem<T>(p, a, o, c);
-    tgamma[static_cast<int64_t>(o) * p.C + c] = w * m;
-    tbeta[static_cast<int64_t>(o) * p.C + c] = w * s;
+    if (c < p.C) {
+      const float* src = mpart + static_cast<int64_t>(o) * p.C + c;
+      const int64_t rstride = static_cast<int64_t>(po) * p.C;
+#pragma unroll 4
+      for (int r = slot; r < ranges; r += 4) m += src[r * rstride];
+    }
+    part[threadIdx.x] = m;
+    __syncthreads();
+    if (slot == 0 && c < p.C) {
+      m = ((part[cl] + part[64 + cl]) + part[128 + cl]) + part[192 + cl];
+      const float dw = fmaf(m, a.gamma[c], s * a.beta[c]);
+      if (o < p.n_qkv)
+        a.dw_qkv[static_cast<int64_t>(o) * p.C + c] = dw;
+      else
+        a.dw_bias[static_cast<int64_t>(o - p.n_qkv) * p.C + c] = dw;
+      const float w = w_elem<T>(p, a, o, c);
+      tgamma[static_cast<int64_t>(o) * p.C + c] = w * m;
+      tbeta[static_cast<int64_t>(o) * p.C + c] = w * s;
+    }
+    __syncthreads();
   }
 }
 
+// One workgroup per channel: thread i sums outputs i, i + 256, ... in order, then
+// a fixed pairwise tree over the 256 partial sums.
 __global__ __launch_bounds__(kVecThreads) void bwd_finalize_cols(ProjProblem p, ProjBwdArgs a, const float* tgamma,
                                                                  const float* tbeta) {
-  const int c = blockIdx.x * kVecThreads + threadIdx.x;
-  if (c >= p.C) return;
+  __shared__ float sg[kVecThreads], sb[kVecThreads];
+  const int c = blockIdx.x;
   float g = 0.f, b = 0.f;
-  for (int o = 0; o < p.n_out; ++o) {
+  for (int o = threadIdx.x; o < p.n_out; o += kVecThreads) {
     g += tgamma[static_cast<int64_t>(o) * p.C + c];
     b += tbeta[static_cast<int64_t>(o) * p.C + c];
   }
-  a.dgamma[c] = g;
-  a.dbeta[c] = b;
+  sg[threadIdx.x] = g;
+  sb[threadIdx.x] = b;
+  __syncthreads();
+  for (int w = kVecThreads / 2; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      sg[threadIdx.x] += sg[threadIdx.x + w];
+      sb[threadIdx.x] += sb[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.dgamma[c] = sg[0];
+    a.dbeta[c] = sb[0];
+  }
 }
 
 // ---------------------------------------------------------------- launch
 
 bool use_mfma(const ProjProblem& p) { return p.dtype == 1 && (p.C == 32 || p.C == 64 || p.C == 128); }
 
-int dx_ko(const ProjProblem& p) { return (p.n_out + 15) / 16 * 16; }
+// Outputs the dx kernel contracts over: q/k/v rows, then the bias buffer's
+// columns, rounded up to whole 16-output k-steps.
+int dx_ko(const ProjProblem& p) { return (p.n_qkv + bias_width(p) + 15) / 16 * 16; }
 
 size_t dx_lds_bytes(const ProjProblem& p) {
   return static_cast<size_t>(4) * p.C + static_cast<size_t>(p.C) * (2 * dx_ko(p) + 16);
@@ -526,7 +617,7 @@ size_t dx_lds_bytes(const ProjProblem& p) {
 
 struct WsLayout {
   int ranges, range_chunks;
-  size_t mpart, spart, tgamma, tbeta, total;  // byte offsets
+  size_t mpart, spart, tgamma, tbeta, gb, total;  // byte offsets
 };
 
 WsLayout ws_layout(const ProjProblem& p) {
@@ -538,7 +629,8 @@ WsLayout ws_layout(const ProjProblem& p) {
   w.spart = up(w.mpart + static_cast<size_t>(w.ranges) * po * p.C * sizeof(float));
   w.tgamma = up(w.spart + static_cast<size_t>(w.ranges) * po * sizeof(float));
   w.tbeta = up(w.tgamma + static_cast<size_t>(p.n_out) * p.C * sizeof(float));
-  w.total = up(w.tbeta + static_cast<size_t>(p.n_out) * p.C * sizeof(float));
+  w.gb = up(w.tbeta + static_cast<size_t>(p.n_out) * p.C * sizeof(float));
+  w.total = up(w.gb + static_cast<size_t>(p.T) * bias_width(p) * sizeof(uint16_t));
   return w;
 }
 
@@ -556,17 +648,50 @@ hipError_t persistent_grid(K kern, size_t lds, int want, int* grid) {
   return hipSuccess;
 }
 
+// The dx kernels: MFMA when q/k/v rows are 32, 64 or 128 wide (and at most 16
+// bias heads, and the weights fit in LDS), else the vector kernel.
+bool dx_mfma_shape(const ProjProblem& p) {
+  const int hd = p.H * p.D;
+  return p.dtype == 1 && (p.C == 32 || p.C == 64 || p.C == 128) && p.n_qkv > 0 && bias_width(p) <= 16 &&
+         (hd == 32 || hd == 64 || hd == 128) && dx_lds_bytes(p) <= kMaxLds;
+}
+
+hipError_t launch_dx_vector(const ProjProblem& p, const ProjBwdArgs& a, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(kVecTokens) * p.C * sizeof(float);
+  const int64_t grid = (p.T + kVecTokens - 1) / kVecTokens;
+  KernelTimer timer("ln_proj_bwd_dx_vector", s);
+  if (p.dtype == 1)
+    hipLaunchKernelGGL(bwd_dx_vector<uint16_t>, dim3(static_cast<unsigned>(grid)), dim3(kVecThreads), lds, s, p, a);
+  else
+    hipLaunchKernelGGL(bwd_dx_vector<float>, dim3(static_cast<unsigned>(grid)), dim3(kVecThreads), lds, s, p, a);
+  return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_dx(const ProjProblem& p, const ProjBwdArgs& a, const uint16_t* gb, hipStream_t s) {
+  if (!dx_mfma_shape(p)) return launch_dx_vector(p, a, s);
+  const size_t lds = dx_lds_bytes(p);
+  const int hd = p.H * p.D;
+  auto kern = hd == 32 ? bwd_dx_mfma<KS, 2> : (hd == 64 ? bwd_dx_mfma<KS, 4> : bwd_dx_mfma<KS, 8>);
+  int grid = 0;
+  hipError_t e = persistent_grid(kern, lds, (p.tiles + kWaves - 1) / kWaves, &grid);
+  if (e != hipSuccess) return e;
+  KernelTimer timer("ln_proj_bwd_dx", s);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, p, a, gb, dx_ko(p));
+  return hipGetLastError();
+}
+
 template <int KS>
 hipError_t launch_mfma(const ProjProblem& p, const ProjBwdArgs& a, const WsLayout& w, char* ws, hipStream_t s) {
   hipError_t e;
-  {
-    const size_t lds = dx_lds_bytes(p);
-    int grid = 0;
-    if ((e = persistent_grid(bwd_dx_mfma<KS>, lds, (p.tiles + kWaves - 1) / kWaves, &grid)) != hipSuccess) return e;
-    KernelTimer timer("ln_proj_bwd_dx", s);
-    hipLaunchKernelGGL(bwd_dx_mfma<KS>, dim3(grid), dim3(kThreads), lds, s, p, a, dx_ko(p));
+  const uint16_t* gb = reinterpret_cast<const uint16_t*>(ws + w.gb);
+  if (bias_width(p) > 0) {
+    KernelTimer timer("ln_proj_bwd_bias_tokens", s);
+    hipLaunchKernelGGL(bias_grad_tokens, dim3(static_cast<unsigned>((p.T + 255) / 256)), dim3(256), 0, s, p, a,
+                       reinterpret_cast<uint16_t*>(ws + w.gb));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  if ((e = launch_dx<KS>(p, a, gb, s)) != hipSuccess) return e;
   {
     const size_t lds = 2 * static_cast<size_t>(mpart_stage_bytes<KS>());
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_mpart_mfma<KS>),
@@ -574,7 +699,7 @@ hipError_t launch_mfma(const ProjProblem& p, const ProjBwdArgs& a, const WsLayou
     if (e != hipSuccess) return e;
     const int n_groups = ((p.n_out + 31) / 32 + 3) / 4;
     KernelTimer timer("ln_proj_bwd_mpart", s);
-    hipLaunchKernelGGL(bwd_mpart_mfma<KS>, dim3(n_groups * w.ranges), dim3(kThreads), lds, s, p, a, n_groups,
+    hipLaunchKernelGGL(bwd_mpart_mfma<KS>, dim3(n_groups * w.ranges), dim3(kThreads), lds, s, p, a, gb, n_groups,
                        w.ranges, w.range_chunks, reinterpret_cast<float*>(ws + w.mpart),
                        reinterpret_cast<float*>(ws + w.spart));
     return hipGetLastError();
@@ -593,7 +718,7 @@ hipError_t launch_ln_proj_bwd(const ProjProblem& p, const ProjBwdArgs& a, void* 
   float* tgamma = reinterpret_cast<float*>(ws + w.tgamma);
   float* tbeta = reinterpret_cast<float*>(ws + w.tbeta);
   hipError_t e = hipSuccess;
-  const bool mf = use_mfma(p) && dx_lds_bytes(p) <= kMaxLds;
+  const bool mf = use_mfma(p);
   if (mf) {
     switch (p.C) {
       case 32: e = launch_mfma<2>(p, a, w, ws, s); break;
@@ -601,17 +726,8 @@ hipError_t launch_ln_proj_bwd(const ProjProblem& p, const ProjBwdArgs& a, void* 
       default: e = launch_mfma<8>(p, a, w, ws, s); break;
     }
   } else {
-    const size_t lds = static_cast<size_t>(kVecTokens) * p.C * sizeof(float);
-    const int64_t grid = (p.T + kVecTokens - 1) / kVecTokens;
     const int range_tokens = w.range_chunks * kChunk;
-    {
-      KernelTimer timer("ln_proj_bwd_dx_vector", s);
-      if (p.dtype == 1)
-        hipLaunchKernelGGL(bwd_dx_vector<uint16_t>, dim3(static_cast<unsigned>(grid)), dim3(kVecThreads), lds, s, p, a);
-      else
-        hipLaunchKernelGGL(bwd_dx_vector<float>, dim3(static_cast<unsigned>(grid)), dim3(kVecThreads), lds, s, p, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    if ((e = launch_dx_vector(p, a, s)) != hipSuccess) return e;
     KernelTimer timer("ln_proj_bwd_mpart_vector", s);
     if (p.dtype == 1)
       hipLaunchKernelGGL(bwd_mpart_vector<uint16_t>, dim3(p.n_out, w.ranges), dim3(kVecThreads), 0, s, p, a,
@@ -631,8 +747,7 @@ hipError_t launch_ln_proj_bwd(const ProjProblem& p, const ProjBwdArgs& a, void* 
       hipLaunchKernelGGL(bwd_finalize_rows<float>, dim3(p.n_out), dim3(kVecThreads), 0, s, p, a, w.ranges, mpart,
                          spart, tgamma, tbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_finalize_cols, dim3((p.C + kVecThreads - 1) / kVecThreads), dim3(kVecThreads), 0, s, p, a,
-                       tgamma, tbeta);
+    hipLaunchKernelGGL(bwd_finalize_cols, dim3(p.C), dim3(kVecThreads), 0, s, p, a, tgamma, tbeta);
   }
   return hipGetLastError();
 }

@@ -23,13 +23,17 @@ __device__ __forceinline__ int64_t tile_token(const ProjProblem& p, int tile, in
   return a < p.A ? static_cast<int64_t>(a) * p.B + b : -1;
 }
 
+// Position of token tok = a*B + b in one head's plane of the bias [H][A][B]:
+// tok itself, or b*A + a when the bias is transposed (tokens < 2^31).
+__device__ __forceinline__ int64_t bias_pos(const ProjProblem& p, int64_t tok) {
+  if (!p.bias_transpose) return tok;
+  const int t = static_cast<int>(tok);
+  const int a = t / p.B;
+  return static_cast<int64_t>(t - a * p.B) * p.A + a;
+}
+
 __device__ __forceinline__ int64_t bias_offset(const ProjProblem& p, int hb, int64_t tok) {
-  int64_t pos = tok;
-  if (p.bias_transpose) {
-    const int64_t a = tok / p.B;
-    pos = (tok - a * p.B) * p.A + a;
-  }
-  return static_cast<int64_t>(hb) * p.T + pos;
+  return static_cast<int64_t>(hb) * p.T + bias_pos(p, tok);
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }

@@ -62,6 +62,9 @@ KERNEL_SOURCES = {
     "bwd_dkdv_mfma": ["kernels_bwd_dkdv.hip"],
     "bwd_dq_mfma": ["kernels_bwd_dq.hip"],
     "bwd_dbias_mfma": ["kernels_bwd_dbias.hip"],
+    "ln_proj_fwd": ["kernels_ln_proj.hip", "proj_common.h"],
+    "ln_proj_bwd_dx": ["kernels_ln_proj_bwd.hip", "proj_common.h"],
+    "ln_proj_bwd_mpart": ["kernels_ln_proj_bwd.hip", "proj_common.h"],
 }
 
 
@@ -106,7 +109,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first (the GPU clocks take some tens of ms to settle)")
-    ap.add_argument("--workload", default="tri_start_bf16_n384")
+    ap.add_argument("--workload", default="tri_start_bf16_n384",
+                    help="an attention workload, or a layer norm + projection workload "
+                         "(pair_proj_bf16_n384, pair_proj_end_bf16_n768, msa_proj_bf16_s512_n384): "
+                         "the latter prints the projection step's own line")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -118,6 +124,8 @@ def parse():
                     help="instead of the throughput line: peak extra HBM of one fwd+bwd at N = 64 .. 1536 "
                          "(R = N, H = 4, d = 32, bf16), beside a materialised fp32 torch reference until it "
                          "runs out of memory")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="projection workloads: skip the unfused torch layer_norm + mm pipeline timed beside")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the second pass with per-kernel HIP events (no roofline)")
     return ap.parse_args()
@@ -232,6 +240,233 @@ def memory_curve():
                       "config": {"heads": 4, "head_dim": 32, "mask": "tail 5%"}}), flush=True)
 
 
+def copy_calibration(dev):
+    """An elementwise kernel that reads and writes exactly 256 MiB each (negation of a
+    contiguous fp32 tensor), run three times: its FETCH_SIZE and WRITE_SIZE readings
+    give the factor between counter bytes and true HBM bytes."""
+    import torch
+
+    nbytes = 256 << 20
+    src = torch.randn(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    return {"kernel": "torch.neg fp32", "read_bytes": nbytes, "write_bytes": nbytes, "launches": 3}
+
+
+# ---------------------------------------------------------------- layer norm + projections
+
+PROJ_METRIC = "layer norm + q/k/v/bias projections fwd+bwd, effective HBM GB/s"
+
+
+def proj_bytes(w, es):
+    """Algorithmic HBM bytes of the projection step and of each kernel launch.
+
+    The step's bytes are what a single fused pass must move: forward x in, q, k, v,
+    bias and the statistics out; backward x, the upstream gradients (dbias in fp32)
+    and the statistics in, dx out; weights and their gradients once each."""
+    T, C, H = w.tokens, w.channels, w.heads
+    n_qkv = 3 * H * w.head_dim if w.qkv else 0
+    nb = H if w.bias else 0
+    n_out = n_qkv + nb
+    weights = n_out * C * es + 2 * C * 4
+    fwd = T * C * es + T * n_qkv * es + T * nb * es + T * 8 + weights
+    grads_in = T * n_qkv * es + T * nb * 4
+    hb = -(-nb // 8) * 8
+    gb = T * hb * 2  # the bias gradient in token order, bf16, written once and read by dx and mpart
+    bwd_dx = T * C * es + T * n_qkv * es + gb + T * 8 + T * C * es + weights
+    chunks = -(-T // 128)
+    ranges = min(64, chunks)
+    per = -(-chunks // ranges)
+    ranges = -(-chunks // per)
+    po = -(-n_out // 32) * 32
+    partial = ranges * po * (C + 1) * 4
+    bwd_mpart = T * C * es + T * n_qkv * es + gb + T * 8 + partial
+    step = fwd + (T * C * es + grads_in + T * 8 + T * C * es) + weights + n_out * C * 4 + 2 * C * 4
+    return step, {"ln_proj_fwd": fwd, "ln_proj_bwd_dx": bwd_dx, "ln_proj_bwd_mpart": bwd_mpart,
+                  "ln_proj_bwd_finalize": partial + 3 * n_out * C * 4, "ln_proj_bwd_bias_tokens": T * nb * 4 + gb}
+
+
+def proj_cpu_baseline(w, inp, target_s):
+    """The fp64 oracle (fwd + bwd) on an s x s token sub-grid sized to ~target_s seconds."""
+    import numpy as np
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    f = lambda t: None if t is None else t.detach().cpu().double().numpy()
+    H, D, bt = w.heads, w.head_dim, w.bias_transpose
+
+    def run(s):
+        sub = lambda t: None if t is None else t[:s, :s]
+        x = f(sub(inp["x"]))
+        t0 = time.perf_counter()
+        oracle.ln_proj_fwd(x, f(inp["gamma"]), f(inp["beta"]), inp["eps"], f(inp["w_qkv"]), f(inp["w_bias"]),
+                           H, D, bt)
+        oracle.ln_proj_bwd(x, f(inp["gamma"]), f(inp["beta"]), inp["eps"], f(inp["w_qkv"]), f(inp["w_bias"]),
+                           H, D, bt, f(sub(inp["dq"])), f(sub(inp["dk"])), f(sub(inp["dv"])),
+                           None if inp["dbias"] is None else f(inp["dbias"][:, :s, :s]))
+        return time.perf_counter() - t0
+
+    side = min(w.a, w.b)
+    s, secs = 16, run(16)
+    for _ in range(3):
+        if secs >= 0.6 * target_s or s >= side:
+            break
+        s = int(min(side, max(s + 1, s * (target_s / max(secs, 1e-6)) ** 0.5)))
+        secs = run(s)
+    # A host that finishes the whole grid early repeats it.
+    reps = 1
+    if s >= side and secs < 0.6 * target_s:
+        reps = int(min(20, max(2, round(target_s / max(secs, 1e-6)))))
+        secs = sum(run(s) for _ in range(reps))
+    sample = type(w)(w.name, s, s, w.channels, w.heads, w.head_dim, w.dtype, w.qkv, w.bias, w.bias_transpose)
+    step_bytes, _ = proj_bytes(sample, 2 if w.dtype == "bf16" else 4)
+    return {"value": step_bytes * reps / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{s} x {s} token sub-grid of {w.name} (fwd+bwd, fp64)"
+                      + (f" x {reps} passes" if reps > 1 else "") + f", {secs:.2f} s", "seconds": secs}
+
+
+def proj_main(args, w):
+    import torch
+    import af3_attention_amd as ea
+    from af3_attention_amd import _lib
+    from workloads import generate_proj_workload
+
+    dev = torch.device("cuda:0")
+    es = 2 if w.dtype == "bf16" else 4
+    inp_cpu = generate_proj_workload(w, seed=args.seed)
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp_cpu.items()}
+    H, D, bt = w.heads, w.head_dim, w.bias_transpose
+    ws = torch.empty(ea.ln_proj_bwd_workspace_bytes(w.a, w.b, w.channels, H, D, w.torch_dtype, w.qkv, w.bias),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        fw = ea.ln_proj_fwd(g["x"], g["gamma"], g["beta"], g["w_qkv"], g["w_bias"], heads=H, head_dim=D,
+                            bias_transpose=bt, eps=g["eps"])
+        ea.ln_proj_bwd(g["x"], g["gamma"], g["beta"], g["w_qkv"], g["w_bias"], fw["mean"], fw["rstd"], g["dq"],
+                       g["dk"], g["dv"], g["dbias"], heads=H, head_dim=D, bias_transpose=bt, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, kernel_timing=False):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        _lib.timing_collect()
+        _lib.timing_enable(kernel_timing)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        _lib.timing_enable(False)
+        return start.elapsed_time(stop) / args.steps, _lib.timing_collect()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    base_mem = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ms, _ = timed(step)
+    peak_fused = torch.cuda.max_memory_allocated(dev) - base_mem
+    kernels = {}
+    if not args.no_kernel_timing:
+        _, kernels = timed(step, True)
+    step_bytes, kbytes = proj_bytes(w, es)
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    roofline = None
+    if kernels:
+        name, (count, tot) = max(kernels.items(), key=lambda kv: kv[1][1])
+        avg_ms = tot / count
+        if name in kbytes:
+            achieved = kbytes[name] / (avg_ms * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": achieved / PEAK_HBM_GBS, "traffic": recorded_traffic(name, w.name),
+                        "kernel": name, "avg_launch_ms": avg_ms, "launches": count,
+                        "algorithmic_bytes": kbytes[name]}
+
+    unfused = None
+    if not args.no_unfused:
+        unfused = proj_unfused(w, g, args, stream)
+
+    cpu = None if args.no_cpu_baseline else proj_cpu_baseline(w, inp_cpu, args.cpu_seconds)
+    line = {
+        "metric": PROJ_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "a": w.a, "b": w.b, "channels": w.channels, "heads": H, "head_dim": D,
+                   "qkv": w.qkv, "bias": w.bias, "bias_transpose": bt, "seed": args.seed},
+        "tokens_per_s": w.tokens / (ms * 1e-3),
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "unfused_torch": unfused,
+        "kernels_ms_per_step": {k: tot / args.steps for k, (c, tot) in kernels.items()},
+        "peak_hbm_extra_bytes": int(peak_fused),
+    }
+    if args.copy_calibration:
+        line["copy_calibration"] = copy_calibration(dev)
+    print(json.dumps(line), flush=True)
+
+
+def proj_unfused(w, g, args, stream):
+    """The same step as separate torch kernels (bf16 layer norm, then one mm per
+    projection; backward by mm and the layer-norm backward), which materialise
+    the normalised tensor and its gradient in HBM.  Only 2-D products are used."""
+    import torch
+
+    T, C, H = w.tokens, w.channels, w.heads
+    hd = H * w.head_dim
+    dt = w.torch_dtype
+    dev = g["x"].device
+    x2 = g["x"].view(T, C)
+    gam, bet = g["gamma"].to(dt), g["beta"].to(dt)
+    ws = []
+    if w.qkv:
+        ws += [g["w_qkv"][i * hd:(i + 1) * hd].contiguous() for i in range(3)]
+    if w.bias:
+        ws.append(g["w_bias"].contiguous())
+    wts = [x.t().contiguous() for x in ws]
+    grads = []
+    if w.qkv:
+        grads += [g[n].view(T, hd) for n in ("dq", "dk", "dv")]
+    if w.bias:
+        db = g["dbias"].transpose(1, 2) if w.bias_transpose else g["dbias"]
+        grads.append(db.reshape(H, T).t().contiguous().to(dt))
+
+    def step():
+        y, mean, rstd = torch.native_layer_norm(x2, (C,), gam, bet, g["eps"])
+        outs = [torch.mm(y, wt) for wt in wts]
+        if w.bias:
+            b = outs[-1].t().contiguous()
+            if w.bias_transpose:
+                b = b.view(H, w.a, w.b).transpose(1, 2).contiguous()
+        dy = torch.mm(grads[0], ws[0])
+        for gr, wm in zip(grads[1:], ws[1:]):
+            dy.addmm_(gr, wm)
+        dws = [torch.mm(gr.t(), y) for gr in grads]
+        torch.ops.aten.native_layer_norm_backward(dy, x2, (C,), mean, rstd, gam, bet, [True, True, True])
+        return dws
+
+    for _ in range(max(5, args.warmup // 10)):
+        step()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    return {"ms_per_step": ms, "peak_hbm_extra_bytes": int(torch.cuda.max_memory_allocated(dev) - base),
+            "ops": "native_layer_norm, mm per projection, addmm, mm (weight grads), native_layer_norm_backward"}
+
+
 def main():
     args = parse()
     if args.memory_curve and args.gpus == 1:
@@ -241,6 +476,11 @@ def main():
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+
+    from workloads import PROJ_WORKLOADS
+    if args.workload in PROJ_WORKLOADS:
+        proj_main(args, PROJ_WORKLOADS[args.workload])
+        return
 
     import torch
     import af3_attention_amd as ea
@@ -327,20 +567,7 @@ def main():
                         "frac": achieved / peak, "traffic": recorded_traffic(name, w.name), "kernel": name,
                         "avg_launch_ms": avg_ms, "launches": count}
 
-    calibration = None
-    if args.copy_calibration:
-        # An elementwise kernel that reads and writes exactly `nbytes` each (negation
-        # of a contiguous fp32 tensor): its FETCH_SIZE and WRITE_SIZE readings give
-        # the factor between counter bytes and true HBM bytes.
-        nbytes = 256 << 20
-        src = torch.randn(nbytes // 4, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        calibration = {"kernel": "torch.neg fp32", "read_bytes": nbytes, "write_bytes": nbytes, "launches": 3}
-        del src, dst
+    calibration = copy_calibration(dev) if args.copy_calibration else None
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -274,7 +274,7 @@ def proj_bytes(w, es):
     weights = n_out * C * es + 2 * C * 4
     fwd = T * C * es + T * n_qkv * es + T * nb * es + T * 8 + weights
     grads_in = T * n_qkv * es + T * nb * 4
-    hb = -(-nb // 8) * 8
+    hb = -(-nb // 16) * 16
     gb = T * hb * 2  # the bias gradient in token order, bf16, written once and read by dx and mpart
     bwd_dx = T * C * es + T * n_qkv * es + gb + T * 8 + T * C * es + weights
     chunks = -(-T // 128)
@@ -319,7 +319,7 @@ def proj_cpu_baseline(w, inp, target_s):
     # A host that finishes the whole grid early repeats it.
     reps = 1
     if s >= side and secs < 0.6 * target_s:
-        reps = int(min(20, max(2, round(target_s / max(secs, 1e-6)))))
+        reps = int(min(60, max(2, round(target_s / max(secs, 1e-6)))))
         secs = sum(run(s) for _ in range(reps))
     sample = type(w)(w.name, s, s, w.channels, w.heads, w.head_dim, w.dtype, w.qkv, w.bias, w.bias_transpose)
     step_bytes, _ = proj_bytes(sample, 2 if w.dtype == "bf16" else 4)

@@ -246,12 +246,15 @@ def test_ln_proj_bwd_validation(kw, code, needle):
 
 def test_ln_proj_bwd_workspace_query():
     lib = _lib.load()
-    n = lib.evoattn_ln_proj_bwd_workspace_bytes(384, 384, 128, 4, 32, 1, 1, 1)
-    assert n % 256 == 0
-    # partial sums over at most 64 token ranges of a (3*H*d + H, padded to 32) x C array, plus two
-    # (3*H*d + H) x C product arrays: independent of N beyond the range count
-    assert n <= 64 * 416 * 128 * 4 + 64 * 416 * 4 + 2 * 388 * 128 * 4 + 4 * 256
-    assert n == lib.evoattn_ln_proj_bwd_workspace_bytes(1536, 1536, 128, 4, 32, 1, 1, 1)
+    fixed = 64 * 416 * 128 * 4 + 64 * 416 * 4 + 2 * 388 * 128 * 4 + 5 * 256
+    for n_tok in (384, 1536):
+        n = lib.evoattn_ln_proj_bwd_workspace_bytes(n_tok, n_tok, 128, 4, 32, 1, 1, 1)
+        assert n % 256 == 0
+        # partial sums over at most 64 token ranges of a (3*H*d + H, padded to 32) x C array, two
+        # (3*H*d + H) x C product arrays, and the pair-bias gradient in token order (16 bf16 per token)
+        assert n_tok * n_tok * 16 * 2 <= n <= fixed + n_tok * n_tok * 16 * 2
+    # without the bias there is no token-order buffer
+    assert lib.evoattn_ln_proj_bwd_workspace_bytes(1536, 1536, 128, 4, 32, 1, 1, 0) <= fixed
     assert lib.evoattn_ln_proj_bwd_workspace_bytes(8, 9, 128, 4, 32, 1, 1, 1) == 0   # bias needs a == b
     assert lib.evoattn_ln_proj_bwd_workspace_bytes(8, 8, 128, 4, 32, 1, 0, 0) == 0   # nothing to project
 

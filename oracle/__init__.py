@@ -140,3 +140,4 @@ def bwd(q, k, v, bias, mask, dout, transpose=0, rows=None):
 
 
 from .ln_proj import layer_norm, ln_proj_bwd, ln_proj_fwd  # noqa: E402,F401
+from .transition import silu, silu_grad, transition_bwd, transition_fwd  # noqa: E402,F401

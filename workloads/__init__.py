@@ -248,3 +248,83 @@ def generate_proj_workload(w: ProjWorkload, *, seed: int = 0, device="cpu"):
                         qkv=w.qkv, bias=w.bias, seed=seed, device=device)
     out["bias_transpose"] = w.bias_transpose
     return out
+
+
+# ---------------------------------------------------------------- SwiGLU transition
+
+@dataclass(frozen=True)
+class TransitionWorkload:
+    """Layer norm, two expansions to n*C hidden units, silu(a)*b, projection back to C."""
+    name: str
+    a: int
+    b: int
+    channels: int
+    expansion: int
+    dtype: str
+    desc: str = ""
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    @property
+    def tokens(self) -> int:
+        return self.a * self.b
+
+    @property
+    def hidden(self) -> int:
+        return self.expansion * self.channels
+
+    def flops_fwd(self) -> float:
+        """Three T x C x nC products (two expansions, one projection)."""
+        return 2.0 * 3 * self.tokens * self.channels * self.hidden
+
+    def flops_fwd_bwd(self) -> float:
+        """Forward 3, backward 6 products (dh, dy from da and db, and the three weight
+        gradients); the a, b recompute of the backward is not counted."""
+        return 2.0 * 9 * self.tokens * self.channels * self.hidden
+
+
+TRANSITION_WORKLOADS = {
+    "pair_transition_fp32_n48": TransitionWorkload(
+        "pair_transition_fp32_n48", 48, 48, 128, 4, "fp32", "pair tensor N=48, C=128, n=4, fp32"),
+    # The pair transition at the headline crop (N=384, C=128, 512 hidden units).
+    "pair_transition_bf16_n384": TransitionWorkload(
+        "pair_transition_bf16_n384", 384, 384, 128, 4, "bf16", "pair tensor N=384, C=128, n=4, bf16"),
+    "msa_transition_bf16_s512_n384": TransitionWorkload(
+        "msa_transition_bf16_s512_n384", 512, 384, 64, 4, "bf16", "MSA tensor S=512 N=384, C=64, n=4, bf16"),
+}
+
+
+def generate_transition(a: int, b: int, channels: int, expansion: int, *, dtype=torch.bfloat16, seed: int = 0,
+                        device="cpu"):
+    """Draw one seeded input set for the transition.
+
+    Draw order with one torch CPU generator: x, per-token scale, per-token offset,
+    gamma, beta, w_a, w_b, w_out, dout.  x, gamma and beta as for the projections;
+    w_a, w_b ~ N(0, 1/C) and w_out ~ N(0, 1/(n*C)) (fan-in scaling) in the compute
+    dtype; dout ~ N(0, 1)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    hidden = expansion * channels
+    x = torch.randn((a, b, channels), generator=gen, dtype=torch.float32)
+    scale = torch.exp(0.5 * torch.randn((a, b, 1), generator=gen, dtype=torch.float32))
+    offset = torch.randn((a, b, 1), generator=gen, dtype=torch.float32)
+    x = x * scale + offset
+    gamma = 1.0 + 0.1 * torch.randn(channels, generator=gen, dtype=torch.float32)
+    beta = 0.1 * torch.randn(channels, generator=gen, dtype=torch.float32)
+    w_a = torch.randn((hidden, channels), generator=gen, dtype=torch.float32) / math.sqrt(channels)
+    w_b = torch.randn((hidden, channels), generator=gen, dtype=torch.float32) / math.sqrt(channels)
+    w_out = torch.randn((channels, hidden), generator=gen, dtype=torch.float32) / math.sqrt(hidden)
+    dout = torch.randn((a, b, channels), generator=gen, dtype=torch.float32)
+
+    def cast(t, dt=dtype):
+        return t.to(dt).to(device).contiguous()
+
+    return {"x": cast(x), "gamma": cast(gamma, torch.float32), "beta": cast(beta, torch.float32),
+            "w_a": cast(w_a), "w_b": cast(w_b), "w_out": cast(w_out), "dout": cast(dout), "eps": 1e-5,
+            "expansion": expansion}
+
+
+def generate_transition_workload(w: TransitionWorkload, *, seed: int = 0, device="cpu"):
+    return generate_transition(w.a, w.b, w.channels, w.expansion, dtype=w.torch_dtype, seed=seed, device=device)

@@ -19,6 +19,7 @@ EXPORTS = (
     "evoattn_ln_proj_fwd",
     "evoattn_ln_proj_bwd_workspace_bytes",
     "evoattn_ln_proj_bwd",
+    "evoattn_transition_fwd",
 )
 
 _lib = None
@@ -60,6 +61,9 @@ def load():
     lib.evoattn_ln_proj_bwd.argtypes = [i64, i64, i64, i64, i64, c_int, c_int, vp, fp, fp, vp, vp, fp, fp,
                                         vp, vp, vp, fp, vp, fp, fp, fp, fp, vp, sz, vp]
     lib.evoattn_ln_proj_bwd.restype = c_int
+    lib.evoattn_transition_fwd.argtypes = [i64, i64, i64, i64, c_int, ctypes.c_float, vp, fp, fp, vp, vp, vp, vp,
+                                           fp, fp, vp]
+    lib.evoattn_transition_fwd.restype = c_int
     lib.evoattn_timing_enable.argtypes = [c_int]
     lib.evoattn_timing_enable.restype = None
     lib.evoattn_timing_collect.argtypes = [c_int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),

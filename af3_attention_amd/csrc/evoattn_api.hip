@@ -135,6 +135,37 @@ evoattn_status_t check_proj(int64_t A, int64_t B, int64_t C, int64_t heads, int6
   return EVOATTN_OK;
 }
 
+// Validates the SwiGLU transition problem; fills `p`.
+evoattn_status_t check_transition(int64_t A, int64_t B, int64_t C, int64_t expansion, int dtype, float eps,
+                                  evo::TransProblem* p) {
+  if (A < 1 || B < 1 || C < 1 || expansion < 1)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (a=%lld b=%lld channels=%lld expansion=%lld)",
+                (long long)A, (long long)B, (long long)C, (long long)expansion);
+  if (dtype != EVOATTN_FP32 && dtype != EVOATTN_BF16)
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "dtype %d is not EVOATTN_FP32 or EVOATTN_BF16", dtype);
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0, got %g", (double)eps);
+  if (dtype != EVOATTN_BF16)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "the transition is implemented for bf16 only");
+  if (C != 64 && C != 128)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "channels %lld not supported (64 or 128)", (long long)C);
+  if (expansion > 16)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "expansion %lld not supported (1..16)", (long long)expansion);
+  const double T = static_cast<double>(A) * B;
+  if (T * C >= 2147483648.0 || T * C * expansion >= 4294967296.0)
+    return fail(EVOATTN_ERR_UNSUPPORTED, "problem too large: tokens=%.0f", T);
+  if (p) {
+    p->A = static_cast<int>(A);
+    p->B = static_cast<int>(B);
+    p->C = static_cast<int>(C);
+    p->hidden = static_cast<int>(expansion * C);
+    p->T = A * B;
+    p->tiles = static_cast<int>((A * B + 31) / 32);
+    p->eps = eps;
+  }
+  return EVOATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -323,6 +354,32 @@ evoattn_status_t evoattn_ln_proj_bwd(int64_t a, int64_t b, int64_t channels, int
   hipError_t e = evo::launch_ln_proj_bwd(p, args, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(EVOATTN_ERR_DEVICE, "layer norm + projection backward launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return EVOATTN_OK;
+}
+
+evoattn_status_t evoattn_transition_fwd(int64_t a, int64_t b, int64_t channels, int64_t expansion, int dtype,
+                                        float eps, const void* x, const float* gamma, const float* beta,
+                                        const void* w_a, const void* w_b, const void* w_out, void* out, float* mean,
+                                        float* rstd, void* stream) {
+  evo::TransProblem p;
+  evoattn_status_t st = check_transition(a, b, channels, expansion, dtype, eps, &p);
+  if (st != EVOATTN_OK) return st;
+  REQUIRE_PTR(x, 16);
+  REQUIRE_PTR(gamma, 4);
+  REQUIRE_PTR(beta, 4);
+  REQUIRE_PTR(w_a, 16);
+  REQUIRE_PTR(w_b, 16);
+  REQUIRE_PTR(w_out, 16);
+  REQUIRE_PTR(out, 16);
+  if ((mean == nullptr) != (rstd == nullptr))
+    return fail(EVOATTN_ERR_INVALID_ARGUMENT, "mean and rstd must both be given or both be NULL");
+  OPTIONAL_PTR(mean, 4);
+  OPTIONAL_PTR(rstd, 4);
+  if ((st = check_device()) != EVOATTN_OK) return st;
+  evo::TransFwdArgs args{x, gamma, beta, w_a, w_b, w_out, out, mean, rstd};
+  hipError_t e = evo::launch_transition_fwd(p, args, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "transition launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return EVOATTN_OK;
 }

@@ -139,6 +139,50 @@ struct ProjBwdArgs {
 size_t ln_proj_bwd_workspace_bytes(const ProjProblem& p);
 hipError_t launch_ln_proj_bwd(const ProjProblem& p, const ProjBwdArgs& a, void* ws, hipStream_t s);
 
+// SwiGLU transition of a token tensor x [A, B, C] (kernels_transition*.hip):
+// out = (silu(y w_a^T) * (y w_b^T)) w_out^T with y the layer norm of x.
+struct TransProblem {
+  int A, B, C;
+  int hidden;  // expansion * C
+  int64_t T;   // tokens A*B
+  int tiles;   // 32-token tiles
+  float eps;
+};
+
+struct TransFwdArgs {
+  const void* x;
+  const float* gamma;
+  const float* beta;
+  const void* w_a;    // [hidden][C]
+  const void* w_b;    // [hidden][C]
+  const void* w_out;  // [C][hidden]
+  void* out;          // [T][C]
+  float* mean;        // [T] or nullptr
+  float* rstd;        // [T] or nullptr
+};
+
+struct TransBwdArgs {
+  const void* x;
+  const float* gamma;
+  const float* beta;
+  const void* w_a;
+  const void* w_b;
+  const void* w_out;
+  const float* mean;
+  const float* rstd;
+  const void* dout;   // [T][C]
+  void* dx;           // [T][C]
+  float* dgamma;      // [C]
+  float* dbeta;       // [C]
+  float* dw_a;        // [hidden][C]
+  float* dw_b;        // [hidden][C]
+  float* dw_out;      // [C][hidden]
+};
+
+hipError_t launch_transition_fwd(const TransProblem& p, const TransFwdArgs& a, hipStream_t s);
+size_t transition_bwd_workspace_bytes(const TransProblem& p);
+hipError_t launch_transition_bwd(const TransProblem& p, const TransBwdArgs& a, void* ws, hipStream_t s);
+
 // bf16 storage conversions (round to nearest even; NaN stays NaN).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -126,3 +126,32 @@ def ln_proj(x, gamma, beta, w_qkv=None, w_bias=None, *, heads: int, head_dim: in
             eps: float = 1e-5):
     """Differentiable layer norm + projections: returns (q, k, v, bias), None where absent."""
     return LNProjFunction.apply(x, gamma, beta, w_qkv, w_bias, heads, head_dim, bool(bias_transpose), float(eps))
+
+
+# ---------------------------------------------------------------- transition
+
+def transition_fwd(x, gamma, beta, w_a, w_b, w_out, *, eps: float = 1e-5, need_stats: bool = True):
+    """SwiGLU transition: returns dict out ([A, B, C], x's dtype), mean, rstd (fp32 [A*B] or None)."""
+    lib = _lib.load()
+    if x.dim() != 3:
+        raise ValueError(f"x must be 3-D [A, B, C], got {tuple(x.shape)}")
+    A, B, C = x.shape
+    dev = x.device
+    hidden = w_a.shape[0] if w_a.dim() == 2 else -1
+    if hidden % C != 0 or hidden <= 0:
+        raise ValueError(f"w_a must be [n*C, C], got {tuple(w_a.shape)}")
+    _check(x, "x", x.shape, x.dtype, dev)
+    _check(gamma, "gamma", (C,), torch.float32, dev)
+    _check(beta, "beta", (C,), torch.float32, dev)
+    _check(w_a, "w_a", (hidden, C), x.dtype, dev)
+    _check(w_b, "w_b", (hidden, C), x.dtype, dev)
+    _check(w_out, "w_out", (C, hidden), x.dtype, dev)
+    out = {"out": torch.empty_like(x), "mean": None, "rstd": None}
+    if need_stats:
+        out["mean"] = torch.empty(A * B, dtype=torch.float32, device=dev)
+        out["rstd"] = torch.empty(A * B, dtype=torch.float32, device=dev)
+    st = lib.evoattn_transition_fwd(A, B, C, hidden // C, _DTYPES[x.dtype], float(eps), _ptr(x), _ptr(gamma),
+                                    _ptr(beta), _ptr(w_a), _ptr(w_b), _ptr(w_out), _ptr(out["out"]),
+                                    _ptr(out["mean"]), _ptr(out["rstd"]), _stream(dev))
+    _lib.check(st, "evoattn_transition_fwd")
+    return out

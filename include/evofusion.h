@@ -97,6 +97,27 @@ evoattn_status_t evoattn_ln_proj_bwd(int64_t a, int64_t b, int64_t channels, int
                                      void* dx, float* dgamma, float* dbeta, float* dw_qkv, float* dw_bias,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- transition
+ * The SwiGLU transition of a pair or MSA tensor (MegaFold, gist.science
+ * technical summary, Methodik section 3 "EvoFusion": SwiGLU is one of the fused
+ * operators; no formula is printed, this is the plainest reading).  For every
+ * token t of x [A, B, C], with y the layer norm above (biased variance, eps in
+ * the square root, per-channel gamma and beta):
+ *
+ *   a[t,j] = sum_c y[t,c] w_a[j,c],   b[t,j] = sum_c y[t,c] w_b[j,c]   (j < n*C)
+ *   h[t,j] = silu(a[t,j]) * b[t,j],   silu(z) = z / (1 + exp(-z))
+ *   out[t,c] = sum_j h[t,j] w_out[c,j]
+ *
+ * Layouts: x, out [A][B][C]; w_a, w_b [n*C][C]; w_out [C][n*C] (torch Linear
+ * weights); gamma, beta [C] fp32; mean, rstd [A*B] fp32.  bf16 only (y and h are
+ * rounded to bf16 as matrix-core operands; sums and statistics are fp32), C in
+ * {64, 128}, expansion n in 1..16.  Other shapes return EVOATTN_ERR_UNSUPPORTED.
+ * y, a, b and h are never written to memory. */
+evoattn_status_t evoattn_transition_fwd(int64_t a, int64_t b, int64_t channels, int64_t expansion, int dtype,
+                                        float eps, const void* x, const float* gamma, const float* beta,
+                                        const void* w_a, const void* w_b, const void* w_out, void* out,
+                                        float* mean, float* rstd, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,124 @@
+"""GPU parity of the fused SwiGLU transition against the fp64 oracle, on the same
+seeded inputs, through the C ABI.
+
+Forward tolerance per output element, from the arithmetic (bf16 has 8
+significant bits, so each rounding moves a value by at most 2^-8 of it):
+  y is rounded to bf16, so a and b move by at most Ea = 2^-8 sum_c |y||w_a| and
+  Eb = 2^-8 sum_c |y||w_b|; h = silu(a) b then moves by at most
+  Eh = |silu'(a)| Ea |b| + |silu(a)| Eb (first order) plus its own rounding to bf16,
+  2^-8 |h|; out = sum_j h_j w_out[c, j] moves by sum_j Eh_j |w_out[c, j]| and by
+  its final rounding 2^-8 |out|.  The test allows 1.25x that bound (second-order
+  terms, the fp32 sums and the hardware exp / reciprocal) plus 1e-6.  The bound
+  sums worst cases over n*C terms, so the test also requires max|err| <= 1e-2
+  max|ref|: the output's own rounding is 2^-8 (0.4 %) and the upstream rounding
+  errors, independent across the n*C terms, add a few tenths of a percent.
+mean: within 1e-6 max|x| + 1e-6; rstd: relative 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import TRANSITION_WORKLOADS, generate_transition, generate_transition_workload
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -8
+
+
+def banner(msg):
+    print(f"\n[transition] {msg}", flush=True)
+
+
+def f64(t):
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def gpu_fwd(inp):
+    import af3_attention_amd as ea
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    out = ea.transition_fwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"], eps=inp["eps"])
+    torch.cuda.synchronize()
+    return out
+
+
+def fwd_bound(x, gamma, beta, eps, wa, wb, wo):
+    """Per-element forward error bound (see the module docstring)."""
+    A, B, C = x.shape
+    y, _, _, _ = oracle.layer_norm(x, gamma, beta, eps)
+    y2 = y.reshape(-1, C)
+    a, b = y2 @ wa.T, y2 @ wb.T
+    h = oracle.silu(a) * b
+    Ea = U * (np.abs(y2) @ np.abs(wa).T)
+    Eb = U * (np.abs(y2) @ np.abs(wb).T)
+    Eh = np.abs(oracle.silu_grad(a)) * Ea * np.abs(b) + np.abs(oracle.silu(a)) * Eb + U * np.abs(h)
+    out = h @ wo.T
+    return (1.25 * (Eh @ np.abs(wo).T + U * np.abs(out)) + 1e-6).reshape(A, B, C)
+
+
+def check_fwd(inp, ia=None, ib=None):
+    got = gpu_fwd(inp)
+    assert bool(torch.isfinite(got["out"]).all())
+    x = inp["x"]
+    o, mean, rstd = got["out"], got["mean"].view(x.shape[:2]), got["rstd"].view(x.shape[:2])
+    if ia is not None:
+        x, o, mean, rstd = x[ia][:, ib], o[ia][:, ib], mean[ia][:, ib], rstd[ia][:, ib]
+    args = [f64(x), f64(inp["gamma"]), f64(inp["beta"]), inp["eps"], f64(inp["w_a"]), f64(inp["w_b"]),
+            f64(inp["w_out"])]
+    ref = oracle.transition_fwd(*args)
+    tol = fwd_bound(*args)
+    err = np.abs(f64(o) - ref["out"])
+    worst = float((err / tol).max())
+    rel = float(err.max() / np.abs(ref["out"]).max())
+    print({"out err/tol": worst, "max err / max ref": rel}, flush=True)
+    assert np.all(err <= tol), f"out: worst err/tol {worst:.3f}"
+    assert rel <= 1e-2, f"out: max err / max|ref| = {rel:.2e}"
+    assert np.abs(f64(mean) - ref["mean"]).max() <= 1e-6 * np.abs(args[0]).max() + 1e-6
+    assert np.abs(f64(rstd) / ref["rstd"] - 1).max() <= 1e-4
+
+
+@pytest.mark.parametrize("A,B,C,n", [(16, 16, 128, 4), (7, 9, 128, 4), (33, 20, 64, 4), (5, 5, 128, 1),
+                                     (12, 11, 64, 2), (1, 1, 128, 4), (40, 41, 128, 4)])
+def test_fwd_shapes(A, B, C, n):
+    """Ragged tiles and passes (token counts not multiples of 32 or 256), both channel
+    counts, expansions 1, 2 and 4, a single token."""
+    banner(f"fwd A={A} B={B} C={C} n={n}")
+    check_fwd(generate_transition(A, B, C, n, dtype=torch.bfloat16, seed=A * 5 + n))
+
+
+def test_fwd_constant_tokens():
+    """Tokens with equal channels normalise to y = beta (zero variance)."""
+    banner("fwd constant tokens")
+    inp = generate_transition(20, 20, 128, 4, dtype=torch.bfloat16, seed=8)
+    x = inp["x"].clone()
+    x[2] = 1.5
+    x[:, 11] = -3.0
+    inp["x"] = x
+    check_fwd(inp)
+
+
+def sample_axis(n, k, seed):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, n - 1), size=k - 2, replace=False)
+    return torch.as_tensor(np.sort(np.concatenate([[0, n - 1], mid])), dtype=torch.long)
+
+
+@pytest.mark.parametrize("name", ["pair_transition_bf16_n384", "msa_transition_bf16_s512_n384"])
+def test_fwd_workloads_sampled(name):
+    """Full sizes in the benchmark's launch configuration; every output finite, a
+    48 x 48 token sub-grid against the oracle."""
+    w = TRANSITION_WORKLOADS[name]
+    banner("fwd " + name)
+    check_fwd(generate_transition_workload(w), sample_axis(w.a, 48, 1), sample_axis(w.b, 48, 2))
+
+
+def test_fwd_unsupported_shapes_fail_loudly():
+    import af3_attention_amd as ea
+    inp = generate_transition(4, 4, 96, 2, dtype=torch.bfloat16, seed=0)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    with pytest.raises(ea.EvoAttnError, match="channels"):
+        ea.transition_fwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"])
+    f = generate_transition(4, 4, 64, 2, dtype=torch.float32, seed=0)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in f.items()}
+    with pytest.raises(ea.EvoAttnError, match="bf16"):
+        ea.transition_fwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"])

@@ -13,4 +13,5 @@ from .evoattn import (  # noqa: F401
 )
 from ._lib import EvoAttnError, LIB_PATH  # noqa: F401
 from .evofusion import (  # noqa: F401,E402
-    LNProjFunction, ln_proj, ln_proj_bwd, ln_proj_bwd_workspace_bytes, ln_proj_fwd, transition_fwd)
+    LNProjFunction, TransitionFunction, ln_proj, ln_proj_bwd, ln_proj_bwd_workspace_bytes, ln_proj_fwd, transition,
+    transition_bwd, transition_bwd_workspace_bytes, transition_fwd)

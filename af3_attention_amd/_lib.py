@@ -20,6 +20,8 @@ EXPORTS = (
     "evoattn_ln_proj_bwd_workspace_bytes",
     "evoattn_ln_proj_bwd",
     "evoattn_transition_fwd",
+    "evoattn_transition_bwd_workspace_bytes",
+    "evoattn_transition_bwd",
 )
 
 _lib = None
@@ -64,6 +66,11 @@ def load():
     lib.evoattn_transition_fwd.argtypes = [i64, i64, i64, i64, c_int, ctypes.c_float, vp, fp, fp, vp, vp, vp, vp,
                                            fp, fp, vp]
     lib.evoattn_transition_fwd.restype = c_int
+    lib.evoattn_transition_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, c_int]
+    lib.evoattn_transition_bwd_workspace_bytes.restype = sz
+    lib.evoattn_transition_bwd.argtypes = [i64, i64, i64, i64, c_int, vp, fp, fp, vp, vp, vp, fp, fp, vp, vp, fp, fp,
+                                           fp, fp, fp, vp, sz, vp]
+    lib.evoattn_transition_bwd.restype = c_int
     lib.evoattn_timing_enable.argtypes = [c_int]
     lib.evoattn_timing_enable.restype = None
     lib.evoattn_timing_collect.argtypes = [c_int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),

@@ -384,4 +384,46 @@ evoattn_status_t evoattn_transition_fwd(int64_t a, int64_t b, int64_t channels, 
   return EVOATTN_OK;
 }
 
+size_t evoattn_transition_bwd_workspace_bytes(int64_t a, int64_t b, int64_t channels, int64_t expansion, int dtype) {
+  evo::TransProblem p;
+  if (check_transition(a, b, channels, expansion, dtype, 0.f, &p) != EVOATTN_OK) return 0;
+  return round_up(evo::transition_bwd_workspace_bytes(p));
+}
+
+evoattn_status_t evoattn_transition_bwd(int64_t a, int64_t b, int64_t channels, int64_t expansion, int dtype,
+                                        const void* x, const float* gamma, const float* beta, const void* w_a,
+                                        const void* w_b, const void* w_out, const float* mean, const float* rstd,
+                                        const void* dout, void* dx, float* dgamma, float* dbeta, float* dw_a,
+                                        float* dw_b, float* dw_out, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  evo::TransProblem p;
+  evoattn_status_t st = check_transition(a, b, channels, expansion, dtype, 0.f, &p);
+  if (st != EVOATTN_OK) return st;
+  REQUIRE_PTR(x, 16);
+  REQUIRE_PTR(gamma, 4);
+  REQUIRE_PTR(beta, 4);
+  REQUIRE_PTR(w_a, 16);
+  REQUIRE_PTR(w_b, 16);
+  REQUIRE_PTR(w_out, 16);
+  REQUIRE_PTR(mean, 4);
+  REQUIRE_PTR(rstd, 4);
+  REQUIRE_PTR(dout, 16);
+  REQUIRE_PTR(dx, 16);
+  REQUIRE_PTR(dgamma, 4);
+  REQUIRE_PTR(dbeta, 4);
+  REQUIRE_PTR(dw_a, 4);
+  REQUIRE_PTR(dw_b, 4);
+  REQUIRE_PTR(dw_out, 4);
+  const size_t need = round_up(evo::transition_bwd_workspace_bytes(p));
+  if (!workspace || workspace_bytes < need)
+    return fail(EVOATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu at %p", need, workspace_bytes, workspace);
+  if (!aligned(workspace, 256)) return fail(EVOATTN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if ((st = check_device()) != EVOATTN_OK) return st;
+  evo::TransBwdArgs args{x, gamma, beta, w_a, w_b, w_out, mean, rstd, dout, dx, dgamma, dbeta, dw_a, dw_b, dw_out};
+  hipError_t e = evo::launch_transition_bwd(p, args, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "transition backward launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return EVOATTN_OK;
+}
+
 }  // extern "C"

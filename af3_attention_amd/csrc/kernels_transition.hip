@@ -24,33 +24,15 @@
 #include "mfma_common.h"
 #include "pipe_common.h"
 #include "proj_common.h"
+#include "transition_common.h"
 
 namespace evo {
 namespace {
 
 using namespace mfma;
+using namespace trans;
 using proj::hi_bf16;
 using proj::lo_bf16;
-
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kHC = 64;  // hidden units per weight chunk
-
-template <int KS>
-struct TransLayout {
-  static constexpr int C = 16 * KS;
-  static constexpr int PW = 2 * C + 16;    // bytes per w_a / w_b chunk row (one hidden unit)
-  static constexpr int PO = 2 * kHC + 16;  // bytes per w_out chunk row (one channel)
-  static constexpr int WA = 0, WB = kHC * PW, WO = 2 * kHC * PW;
-  static constexpr int CHUNK = 2 * kHC * PW + C * PO;
-  static constexpr int PIECES = 2 * kHC * (C / 8) + C * (kHC / 8);  // 16-byte pieces per chunk
-  static constexpr int NP = (PIECES + kThreads - 1) / kThreads;
-  static constexpr size_t lds_bytes() { return 8 * C + 2 * static_cast<size_t>(CHUNK); }
-};
-
-__device__ __forceinline__ float silu(float a) {
-  return a * __builtin_amdgcn_rcpf(1.f + fast_exp2(-a * kLog2e));
-}
 
 template <int KS>
 __global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem p, TransFwdArgs a) {
@@ -70,48 +52,10 @@ __global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem 
   const int nch = p.hidden / kHC;
   const int npass = (p.tiles + kWaves - 1) / kWaves;
 
-  const uint16_t* wa = static_cast<const uint16_t*>(a.w_a);
-  const uint16_t* wb = static_cast<const uint16_t*>(a.w_b);
-  const uint16_t* wo = static_cast<const uint16_t*>(a.w_out);
-  // This thread's pieces of a weight chunk: source offset (elements) and LDS offset.
-  u32x4 wr[L::NP];
-  auto load_w = [&](int ch) {
-    const int h0 = ch * kHC;
-#pragma unroll
-    for (int i = 0; i < L::NP; ++i) {
-      const int idx = tid + i * kThreads;
-      u32x4 v = {0, 0, 0, 0};
-      if (idx < 2 * kHC * (C / 8)) {
-        const int which = idx / (kHC * (C / 8));
-        const int r = idx - which * (kHC * (C / 8));
-        const int hid = r / (C / 8), piece = r - hid * (C / 8);
-        const uint16_t* src = which ? wb : wa;
-        v = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(h0 + hid) * C + 8 * piece);
-      } else if (idx < L::PIECES) {
-        const int r = idx - 2 * kHC * (C / 8);
-        const int c = r / (kHC / 8), piece = r - c * (kHC / 8);
-        v = *reinterpret_cast<const u32x4*>(wo + static_cast<int64_t>(c) * p.hidden + h0 + 8 * piece);
-      }
-      wr[i] = v;
-    }
-  };
-  auto store_w = [&](int buf) {
-    char* dst = wbuf + buf * L::CHUNK;
-#pragma unroll
-    for (int i = 0; i < L::NP; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < 2 * kHC * (C / 8)) {
-        const int which = idx / (kHC * (C / 8));
-        const int r = idx - which * (kHC * (C / 8));
-        const int hid = r / (C / 8), piece = r - hid * (C / 8);
-        *reinterpret_cast<u32x4*>(dst + (which ? L::WB : L::WA) + hid * L::PW + 16 * piece) = wr[i];
-      } else if (idx < L::PIECES) {
-        const int r = idx - 2 * kHC * (C / 8);
-        const int c = r / (kHC / 8), piece = r - c * (kHC / 8);
-        *reinterpret_cast<u32x4*>(dst + L::WO + c * L::PO + 16 * piece) = wr[i];
-      }
-    }
-  };
+  WeightChunks<KS> wch{static_cast<const uint16_t*>(a.w_a), static_cast<const uint16_t*>(a.w_b),
+                       static_cast<const uint16_t*>(a.w_out), p.hidden, tid};
+  auto load_w = [&](int ch) { wch.load(ch); };
+  auto store_w = [&](int buf) { wch.store(wbuf + buf * L::CHUNK); };
 
   for (int c = tid; c < C; c += kThreads) {
     s_gamma[c] = a.gamma[c];

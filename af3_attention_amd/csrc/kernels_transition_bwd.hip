@@ -1,0 +1,673 @@
+// Backward of the fused SwiGLU transition (kernels_transition.hip).
+//
+// For L = sum out * dout, with y = xhat * gamma + beta the layer norm of x:
+//   dh = dout w_out,  da = dh * b * silu'(a),  db = dh * silu(a)
+//   dy = da w_a + db w_b,  dx = rstd (g - mean_c g - xhat mean_c(g xhat)), g = dy gamma
+//   dw_out = dout^T h,  dw_a = da^T y,  dw_b = db^T y
+// and, since y = xhat gamma + beta, with M_a = da^T xhat, s_a = sum_t da (and the
+// same for b):  dw_a = M_a gamma + s_a (x) beta,
+//   dgamma[c] = sum_j (w_a[j,c] M_a[j,c] + w_b[j,c] M_b[j,c])   (= sum_t dy xhat)
+//   dbeta[c]  = sum_j (w_a[j,c] s_a[j] + w_b[j,c] s_b[j])       (= sum_t dy).
+//
+// Launches (bf16, C in {64, 128}):
+//   1. dx, token by token: the forward's structure (256 tokens per workgroup,
+//      weights streamed through LDS in 64-unit hidden chunks) recomputing a and b,
+//      with dh = w_out^T dout, the gate's derivative in registers, and
+//      dy += w_a^T da + w_b^T db read from the same LDS chunk transposed.
+//   2. Weight-gradient partial sums over fixed token ranges, one workgroup per
+//      (64-unit hidden group, token range): a, b and dh are recomputed with the
+//      tokens on the accumulator rows, so da, db and h leave the registers as
+//      operands whose contraction index is the token; they are exchanged through
+//      LDS and accumulated into M_a, M_b and dout^T h against xhat and dout staged
+//      per 64 tokens.  The hidden groups of one range share an XCD.
+//   3. Finalize: partials summed in increasing range order (fixed slots), dw_a,
+//      dw_b, dw_out, and dgamma / dbeta by fixed-shape sums.
+// Nothing of size tokens x hidden is written to memory; every sum has a fixed order.
+
+#include <hip/hip_runtime.h>
+
+#include "evoattn_internal.h"
+#include "mfma_common.h"
+#include "pipe_common.h"
+#include "proj_common.h"
+#include "transition_common.h"
+
+namespace evo {
+namespace {
+
+using namespace mfma;
+using namespace trans;
+using pipe::lds_addr;
+using pipe::lds_load_tr;
+using pipe::xcd_logical_block;
+using proj::hi_bf16;
+using proj::lo_bf16;
+
+constexpr int kTC = 64;          // tokens per staged chunk of the partial-sum kernel
+constexpr int kMaxRanges = 32;   // token ranges of the partial sums
+constexpr int kFinThreads = 256;
+
+__device__ __forceinline__ float sigmoid_f(float a) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-a * kLog2e)); }
+
+// A operand read transposed from an LDS tile with `pitch` bytes per row:
+// lane gets column c0 + lane % 32 at rows r0 + {4 half + 0..3, 8 + 4 half + 0..3},
+// the row order of accumulator registers 8t..8t+7.
+struct TrRead {
+  int row, col;
+  __device__ __forceinline__ explicit TrRead(int lane) {
+    const int i16 = lane & 15;
+    row = 4 * (lane >> 5) + (i16 >> 2);
+    col = (lane & 16) + 4 * (i16 & 3);
+  }
+  __device__ __forceinline__ u32x4 operator()(uint32_t base, int pitch, int r0, int c0) const {
+    const uint32_t ad = base + (r0 + row) * pitch + (c0 + col) * 2;
+    const u32x2 lo = lds_load_tr(ad);
+    const u32x2 hi = lds_load_tr(ad + 8 * pitch);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
+// ---------------------------------------------------------------- 1. dx
+
+template <int KS>
+__global__ __launch_bounds__(kThreads, 1) void transition_bwd_dx(TransProblem p, TransBwdArgs a) {
+  using L = TransLayout<KS>;
+  constexpr int C = L::C;
+  constexpr int CT = C / 32;
+  extern __shared__ __align__(16) char lds[];
+  float* s_gamma = reinterpret_cast<float*>(lds);
+  float* s_beta = s_gamma + C;
+  char* wbuf = lds + 8 * C;
+  const uint32_t wbuf_a = lds_addr(wbuf);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int li = lane & 31;
+  const int nch = p.hidden / kHC;
+  const int npass = (p.tiles + kWaves - 1) / kWaves;
+  const TrRead tr(lane);
+
+  WeightChunks<KS> wch{static_cast<const uint16_t*>(a.w_a), static_cast<const uint16_t*>(a.w_b),
+                       static_cast<const uint16_t*>(a.w_out), p.hidden, tid};
+  for (int c = tid; c < C; c += kThreads) {
+    s_gamma[c] = a.gamma[c];
+    s_beta[c] = a.beta[c];
+  }
+  const int first = blockIdx.x;
+  if (first < npass) {
+    wch.load(0);
+    wch.store(wbuf);
+  }
+  __syncthreads();
+
+  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+  const uint16_t* dog = static_cast<const uint16_t*>(a.dout);
+  uint16_t* dxg = static_cast<uint16_t*>(a.dx);
+  constexpr float inv_c = 1.0f / C;
+  int buf = 0;
+
+  for (int pass = first; pass < npass; pass += gridDim.x) {
+    const int64_t t = static_cast<int64_t>(pass * kWaves + wave) * 32 + li;
+    const bool valid = t < p.T;
+    const int64_t tok = valid ? t : 0;
+    const float mean = valid ? a.mean[tok] : 0.f;
+    const float rstd = valid ? a.rstd[tok] : 0.f;
+
+    // y as the B operand (k = channel, 8 consecutive per lane half).
+    u32x4 yb[KS];
+    {
+      const u32x4* src = reinterpret_cast<const u32x4*>(xg + tok * C + 8 * half);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 xr = valid ? src[2 * ks] : u32x4{0, 0, 0, 0};
+        const int c0 = 16 * ks + 8 * half;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y0 = fmaf((lo_bf16(xr[i]) - mean) * rstd, s_gamma[c0 + 2 * i], s_beta[c0 + 2 * i]);
+          const float y1 = fmaf((hi_bf16(xr[i]) - mean) * rstd, s_gamma[c0 + 2 * i + 1], s_beta[c0 + 2 * i + 1]);
+          yb[ks][i] = pack_bf16(y0, y1);
+        }
+      }
+    }
+    // dout as the B operand of dh, channels in accumulator-row order:
+    // k-step ks holds 16 ks + {4 half + 0..3, 8 + 4 half + 0..3}.
+    u32x4 db_op[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint16_t* row = dog + tok * C + 16 * ks + 4 * half;
+      const u32x2 lo = valid ? *reinterpret_cast<const u32x2*>(row) : u32x2{0, 0};
+      const u32x2 hi = valid ? *reinterpret_cast<const u32x2*>(row + 8) : u32x2{0, 0};
+      db_op[ks] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+
+    f32x16 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x16{};
+
+    for (int ch = 0; ch < nch; ++ch) {
+      // The next chunk is staged in two halves (one per 32 hidden units) to keep
+      // its registers few.
+      constexpr int NPH = (L::NP + 1) / 2;
+      const bool more = ch + 1 < nch || pass + static_cast<int>(gridDim.x) < npass;
+      const int next = ch + 1 < nch ? ch + 1 : 0;
+      char* nbuf = wbuf + (buf ^ 1) * L::CHUNK;
+      if (more) wch.template load<0, NPH>(next);
+      const char* cw = wbuf + buf * L::CHUNK;
+      const uint32_t cwa = wbuf_a + buf * L::CHUNK;
+#pragma unroll
+      for (int ht = 0; ht < kHC / 32; ++ht) {
+        if (ht == 1 && more) {
+          wch.template store<0, NPH>(nbuf);
+          wch.template load<NPH, L::NP>(next);
+        }
+        // a, b, dh: D[hidden][token] for 32 hidden units.
+        const char* ra = cw + L::WA + (32 * ht + li) * L::PW + 16 * half;
+        const char* rb = cw + L::WB + (32 * ht + li) * L::PW + 16 * half;
+        f32x16 fa = {}, fb = {}, fd = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          fa = mma(*reinterpret_cast<const u32x4*>(ra + 32 * ks), yb[ks], fa);
+          fb = mma(*reinterpret_cast<const u32x4*>(rb + 32 * ks), yb[ks], fb);
+          fd = mma(tr(cwa + L::WO, L::PO, 16 * ks, 32 * ht), db_op[ks], fd);
+          // keeps the compiler from hoisting every k-step's LDS reads (registers)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // da = dh b silu'(a), db = dh silu(a); packed registers 8kk..8kk+7 are the
+        // B operand of k-step kk over hidden 32 ht + 16 kk + (accumulator-row order).
+        u32x4 dab[2], dbb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float va[2], vb[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int v = 8 * kk + 2 * i + e;
+              const float s = sigmoid_f(fa[v]);
+              const float sl = fa[v] * s;
+              va[e] = fd[v] * fb[v] * (s * fmaf(fa[v], 1.f - s, 1.f));
+              vb[e] = fd[v] * sl;
+            }
+            dab[kk][i] = pack_bf16(va[0], va[1]);
+            dbb[kk][i] = pack_bf16(vb[0], vb[1]);
+          }
+        // dy[c][token] += w_a^T da + w_b^T db: A = w^T[c][hidden] read transposed.
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            acc[ct] = mma(tr(cwa + L::WA, L::PW, 32 * ht + 16 * kk, 32 * ct), dab[kk], acc[ct]);
+            acc[ct] = mma(tr(cwa + L::WB, L::PW, 32 * ht + 16 * kk, 32 * ct), dbb[kk], acc[ct]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      if (more) wch.template store<NPH, L::NP>(nbuf);
+      __syncthreads();
+      buf ^= 1;
+    }
+
+    // Layer-norm backward on the token's channels (32 ct + 8 g + 4 half + 0..3).
+    u32x2 xd[CT][4];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        xd[ct][g] = valid ? *reinterpret_cast<const u32x2*>(xg + tok * C + 32 * ct + 8 * g + 4 * half) : u32x2{0, 0};
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 32 * ct + 8 * g + 4 * half + e;
+          const uint32_t u = xd[ct][g][e >> 1];
+          const float xh = (((e & 1) ? hi_bf16(u) : lo_bf16(u)) - mean) * rstd;
+          const float gv = acc[ct][4 * g + e] * s_gamma[c];
+          acc[ct][4 * g + e] = gv;
+          s1 += gv;
+          s2 = fmaf(gv, xh, s2);
+        }
+    s1 = pair_sum(s1) * inv_c;
+    s2 = pair_sum(s2) * inv_c;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t u = xd[ct][g][e >> 1];
+          const float xh = (((e & 1) ? hi_bf16(u) : lo_bf16(u)) - mean) * rstd;
+          acc[ct][4 * g + e] = rstd * (acc[ct][4 * g + e] - s1 - xh * s2);
+        }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int g0 = 2 * pr, g1 = 2 * pr + 1;
+        const f32x16& d = acc[ct];
+        const uint32_t a0 = pack_bf16(d[4 * g0], d[4 * g0 + 1]), a1 = pack_bf16(d[4 * g0 + 2], d[4 * g0 + 3]);
+        const uint32_t b0 = pack_bf16(d[4 * g1], d[4 * g1 + 1]), b1 = pack_bf16(d[4 * g1 + 2], d[4 * g1 + 3]);
+        const auto r0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+        if (valid)
+          *reinterpret_cast<u32x4*>(dxg + tok * C + 32 * ct + 8 * (half ? g0 : g1)) = u32x4{r0[0], r1[0], r0[1], r1[1]};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- 2. weight-gradient partials
+
+template <int KS>
+struct WLayout {
+  using L = TransLayout<KS>;
+  static constexpr int C = L::C;
+  static constexpr int PX = 2 * C + 32;                 // staged token row (xhat or dout), bytes
+  static constexpr int STAGE = 2 * kTC * PX;            // xhat then dout
+  static constexpr int XCH = 4 * 3 * 2 * 64 * 16;       // exchange: job x (da, db, h) x k-step x lane
+  static constexpr int W0 = 8 * C;                      // weights (one chunk)
+  static constexpr int S0 = W0 + L::CHUNK;              // two stages
+  static constexpr int X0 = S0 + 2 * STAGE;             // exchange
+  static constexpr int SUMS = X0 + XCH;                 // 4 jobs x 2 x 32 floats
+  static constexpr size_t bytes() { return static_cast<size_t>(SUMS) + 4 * 2 * 32 * 4; }
+};
+
+template <int KS>
+__global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem p, TransBwdArgs a, int ngroups,
+                                                                   int ranges, int range_chunks, float* ma, float* mb,
+                                                                   float* mo, float* sa, float* sb) {
+  using L = TransLayout<KS>;
+  using W = WLayout<KS>;
+  constexpr int C = L::C;
+  constexpr int CT = C / 32;
+  constexpr int PX = W::PX;
+  constexpr int XPL = C / 8;                     // 16-byte pieces per token row
+  constexpr int NPC = kTC * XPL / kThreads;      // pieces of each tensor per thread
+  constexpr int NT = 3 * 2 * CT;                 // product tiles per workgroup
+  constexpr int TPW = (NT + kWaves - 1) / kWaves;
+  static_assert(kTC * XPL % kThreads == 0, "token pieces must divide evenly");
+  extern __shared__ __align__(16) char lds[];
+  float* s_gamma = reinterpret_cast<float*>(lds);
+  float* s_beta = s_gamma + C;
+  const uint32_t base = lds_addr(lds);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int li = lane & 31;
+  const TrRead tr(lane);
+  const int blk = xcd_logical_block(blockIdx.x, ngroups * ranges);
+  const int group = blk % ngroups;
+  const int range = blk / ngroups;
+  const int64_t t_begin = static_cast<int64_t>(range) * range_chunks * kTC;
+  const int64_t t_end = min(p.T, t_begin + static_cast<int64_t>(range_chunks) * kTC);
+  const int nch = static_cast<int>((t_end - t_begin + kTC - 1) / kTC);
+
+  {
+    WeightChunks<KS> wch{static_cast<const uint16_t*>(a.w_a), static_cast<const uint16_t*>(a.w_b),
+                         static_cast<const uint16_t*>(a.w_out), p.hidden, tid};
+    wch.load(group);
+    wch.store(lds + W::W0);
+    for (int c = tid; c < C; c += kThreads) {
+      s_gamma[c] = a.gamma[c];
+      s_beta[c] = a.beta[c];
+    }
+  }
+
+  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+  const uint16_t* dog = static_cast<const uint16_t*>(a.dout);
+  u32x4 xr[NPC], dr[NPC];
+  float xm[NPC], xs[NPC];
+  auto load = [&](int ch) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(ch) * kTC;
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int idx = tid + i * kThreads;
+      const int t = idx / XPL, j = idx - (idx / XPL) * XPL;
+      const int64_t tok = t0 + t;
+      if (tok < t_end) {
+        xr[i] = *reinterpret_cast<const u32x4*>(xg + tok * C + 8 * j);
+        dr[i] = *reinterpret_cast<const u32x4*>(dog + tok * C + 8 * j);
+        xm[i] = a.mean[tok];
+        xs[i] = a.rstd[tok];
+      } else {
+        xr[i] = dr[i] = u32x4{0, 0, 0, 0};
+        xm[i] = xs[i] = 0.f;
+      }
+    }
+  };
+  auto store = [&](int stage) {
+    char* sx = lds + W::S0 + stage * W::STAGE;
+    char* sd = sx + kTC * PX;
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int idx = tid + i * kThreads;
+      const int t = idx / XPL, j = idx - (idx / XPL) * XPL;
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf16((lo_bf16(xr[i][e]) - xm[i]) * xs[i], (hi_bf16(xr[i][e]) - xm[i]) * xs[i]);
+      *reinterpret_cast<u32x4*>(sx + t * PX + 16 * j) = o;
+      *reinterpret_cast<u32x4*>(sd + t * PX + 16 * j) = dr[i];
+    }
+  };
+  // Exchange slot of (job, quantity 0 da / 1 db / 2 h, k-step) for one lane.
+  auto xslot = [&](int job, int q, int kk) { return W::X0 + ((job * 3 + q) * 2 + kk) * 1024 + 16 * lane; };
+
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
+  float sacc = 0.f, sbcc = 0.f;  // phase-A waves: per-lane partial sums of da and db
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int stage = ch & 1;
+    if (ch + 1 < nch) load(ch + 1);
+    const uint32_t sx = base + W::S0 + stage * W::STAGE;
+    const uint32_t sd = sx + kTC * PX;
+    const char* sxp = lds + W::S0 + stage * W::STAGE;
+    const char* sdp = sxp + kTC * PX;
+
+    // Phase A: waves 0..3 each take (32 hidden units ht, 32 tokens sub) and form
+    // a, b, dh as D[token][hidden], then da, db, h as token-contracted operands.
+    if (wave < 4) {
+      const int ht = wave & 1, sub = wave >> 1;
+      const int trow = sub * 32 + li;
+      const char* wa_row = lds + W::W0 + L::WA + (32 * ht + li) * L::PW + 16 * half;
+      const char* wb_row = lds + W::W0 + L::WB + (32 * ht + li) * L::PW + 16 * half;
+      f32x16 fa = {}, fb = {}, fd = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        // y[token][16 ks + 8 half + 0..7] from the staged xhat row.
+        const u32x4 xh = *reinterpret_cast<const u32x4*>(sxp + trow * PX + 2 * (16 * ks + 8 * half));
+        const int c0 = 16 * ks + 8 * half;
+        u32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          y[i] = pack_bf16(fmaf(lo_bf16(xh[i]), s_gamma[c0 + 2 * i], s_beta[c0 + 2 * i]),
+                           fmaf(hi_bf16(xh[i]), s_gamma[c0 + 2 * i + 1], s_beta[c0 + 2 * i + 1]));
+        fa = mma(y, *reinterpret_cast<const u32x4*>(wa_row + 32 * ks), fa);
+        fb = mma(y, *reinterpret_cast<const u32x4*>(wb_row + 32 * ks), fb);
+        // dout[token][16 ks + accumulator-row order] against w_out read transposed.
+        const char* drow = sdp + trow * PX + 2 * (16 * ks + 4 * half);
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(drow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(drow + 16);
+        fd = mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, tr(base + W::W0 + L::WO, L::PO, 16 * ks, 32 * ht), fd);
+      }
+      // Lane: hidden 32 ht + lane % 32; register v: token sub*32 + accumulator row v.
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 oa, ob, oh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float va[2], vb[2], vh[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int v = 8 * kk + 2 * i + e;
+            const float s = sigmoid_f(fa[v]);
+            const float sl = fa[v] * s;
+            va[e] = fd[v] * fb[v] * (s * fmaf(fa[v], 1.f - s, 1.f));
+            vb[e] = fd[v] * sl;
+            vh[e] = sl * fb[v];
+            sacc += va[e];
+            sbcc += vb[e];
+          }
+          oa[i] = pack_bf16(va[0], va[1]);
+          ob[i] = pack_bf16(vb[0], vb[1]);
+          oh[i] = pack_bf16(vh[0], vh[1]);
+        }
+        const int job = wave;
+        *reinterpret_cast<u32x4*>(lds + xslot(job, 0, kk)) = oa;
+        *reinterpret_cast<u32x4*>(lds + xslot(job, 1, kk)) = ob;
+        *reinterpret_cast<u32x4*>(lds + xslot(job, 2, kk)) = oh;
+      }
+    }
+    __syncthreads();
+
+    // Phase C: product tiles over the chunk's 64 tokens (four 16-token k-steps).
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tl = wave + kWaves * i;
+      if (tl < NT) {
+        const int q = tl / (2 * CT);
+        const int rem = tl - q * (2 * CT);
+        const int ht = rem / CT, ct = rem - (rem / CT) * CT;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int sub = k4 >> 1, kk = k4 & 1;
+          const int job = ht + 2 * sub;
+          if (q < 2) {
+            // M[hidden][c] += (da or db)[hidden][token] xhat[token][c]
+            const u32x4 av = *reinterpret_cast<const u32x4*>(lds + xslot(job, q, kk));
+            acc[i] = mma(av, tr(sx, PX, 32 * sub + 16 * kk, 32 * ct), acc[i]);
+          } else {
+            // Mo[c][hidden] += dout[token][c]^T h[token][hidden]
+            const u32x4 hv = *reinterpret_cast<const u32x4*>(lds + xslot(job, 2, kk));
+            acc[i] = mma(tr(sd, PX, 32 * sub + 16 * kk, 32 * ct), hv, acc[i]);
+          }
+        }
+      }
+    }
+    if (ch + 1 < nch) store(stage ^ 1);
+    __syncthreads();
+  }
+
+  // Partial sums of this range: M_a, M_b [hidden][C], Mo [C][hidden], s_a, s_b [hidden].
+  const int h0 = group * kHC;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tl = wave + kWaves * i;
+    if (tl < NT) {
+      const int q = tl / (2 * CT);
+      const int rem = tl - q * (2 * CT);
+      const int ht = rem / CT, ct = rem - (rem / CT) * CT;
+      if (q < 2) {
+        float* dst = (q == 0 ? ma : mb) + (static_cast<int64_t>(range) * p.hidden + h0 + 32 * ht) * C + 32 * ct + li;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[static_cast<int64_t>(acc_row(v, lane)) * C] = acc[i][v];
+      } else {
+        float* dst = mo + (static_cast<int64_t>(range) * C + 32 * ct) * p.hidden + h0 + 32 * ht + li;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[static_cast<int64_t>(acc_row(v, lane)) * p.hidden] = acc[i][v];
+      }
+    }
+  }
+  float* sums = reinterpret_cast<float*>(lds + W::SUMS);  // [job][a/b][32]
+  if (wave < 4) {
+    const float ta = pair_sum(sacc), tb = pair_sum(sbcc);
+    if (half == 0) {
+      sums[(wave * 2 + 0) * 32 + li] = ta;
+      sums[(wave * 2 + 1) * 32 + li] = tb;
+    }
+  }
+  __syncthreads();
+  if (tid < kHC) {
+    const int ht = tid >> 5, l = tid & 31;
+    // jobs ht (tokens 0..31 of each chunk) then ht + 2 (tokens 32..63)
+    sa[static_cast<int64_t>(range) * p.hidden + h0 + tid] = sums[(ht * 2 + 0) * 32 + l] + sums[((ht + 2) * 2 + 0) * 32 + l];
+    sb[static_cast<int64_t>(range) * p.hidden + h0 + tid] = sums[(ht * 2 + 1) * 32 + l] + sums[((ht + 2) * 2 + 1) * 32 + l];
+  }
+}
+
+// ---------------------------------------------------------------- 3. finalize
+
+__device__ __forceinline__ float bf(const void* p, int64_t i) { return bf16_to_f32(static_cast<const uint16_t*>(p)[i]); }
+
+// One workgroup per hidden unit j: M_a, M_b, s_a, s_b over the ranges (four fixed
+// slots, then in slot order), dw_a, dw_b, and the products whose sums over j are
+// dgamma and dbeta.
+__global__ __launch_bounds__(kFinThreads) void transition_fin_hidden(TransProblem p, TransBwdArgs a, int ranges,
+                                                                    const float* ma, const float* mb, const float* sa,
+                                                                    const float* sb, float* tg, float* tb) {
+  __shared__ float part[2][kFinThreads];
+  const int j = blockIdx.x;
+  const int slot = threadIdx.x >> 6, cl = threadIdx.x & 63;
+  float s_a = 0.f, s_b = 0.f;
+  for (int r = 0; r < ranges; ++r) {
+    s_a += sa[static_cast<int64_t>(r) * p.hidden + j];
+    s_b += sb[static_cast<int64_t>(r) * p.hidden + j];
+  }
+  const int64_t rstride = static_cast<int64_t>(p.hidden) * p.C;
+  for (int c0 = 0; c0 < p.C; c0 += 64) {
+    const int c = c0 + cl;
+    float m_a = 0.f, m_b = 0.f;
+    if (c < p.C) {
+      const int64_t off = static_cast<int64_t>(j) * p.C + c;
+      for (int r = slot; r < ranges; r += 4) {
+        m_a += ma[r * rstride + off];
+        m_b += mb[r * rstride + off];
+      }
+    }
+    part[0][threadIdx.x] = m_a;
+    part[1][threadIdx.x] = m_b;
+    __syncthreads();
+    if (slot == 0 && c < p.C) {
+      m_a = ((part[0][cl] + part[0][64 + cl]) + part[0][128 + cl]) + part[0][192 + cl];
+      m_b = ((part[1][cl] + part[1][64 + cl]) + part[1][128 + cl]) + part[1][192 + cl];
+      const int64_t off = static_cast<int64_t>(j) * p.C + c;
+      a.dw_a[off] = fmaf(m_a, a.gamma[c], s_a * a.beta[c]);
+      a.dw_b[off] = fmaf(m_b, a.gamma[c], s_b * a.beta[c]);
+      const float wa = bf(a.w_a, off), wb = bf(a.w_b, off);
+      tg[off] = fmaf(wa, m_a, wb * m_b);
+      tb[off] = fmaf(wa, s_a, wb * s_b);
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup per channel c: dw_out[c][:] over the ranges in order.
+__global__ __launch_bounds__(kFinThreads) void transition_fin_out(TransProblem p, TransBwdArgs a, int ranges,
+                                                                 const float* mo) {
+  const int c = blockIdx.x;
+  for (int j = threadIdx.x; j < p.hidden; j += kFinThreads) {
+    float s = 0.f;
+    for (int r = 0; r < ranges; ++r) s += mo[(static_cast<int64_t>(r) * p.C + c) * p.hidden + j];
+    a.dw_out[static_cast<int64_t>(c) * p.hidden + j] = s;
+  }
+}
+
+// One workgroup per channel c: dgamma, dbeta as sums over hidden units (thread i
+// takes i, i + 256, ... in order, then a fixed pairwise tree).
+__global__ __launch_bounds__(kFinThreads) void transition_fin_cols(TransProblem p, TransBwdArgs a, const float* tg,
+                                                                  const float* tb) {
+  __shared__ float sg[kFinThreads], sbb[kFinThreads];
+  const int c = blockIdx.x;
+  float g = 0.f, b = 0.f;
+  for (int j = threadIdx.x; j < p.hidden; j += kFinThreads) {
+    g += tg[static_cast<int64_t>(j) * p.C + c];
+    b += tb[static_cast<int64_t>(j) * p.C + c];
+  }
+  sg[threadIdx.x] = g;
+  sbb[threadIdx.x] = b;
+  __syncthreads();
+  for (int w = kFinThreads / 2; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      sg[threadIdx.x] += sg[threadIdx.x + w];
+      sbb[threadIdx.x] += sbb[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.dgamma[c] = sg[0];
+    a.dbeta[c] = sbb[0];
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+struct TWs {
+  int ranges, range_chunks;
+  size_t ma, mb, mo, sa, sb, tg, tb, total;
+};
+
+TWs tws(const TransProblem& p) {
+  TWs w{};
+  const int64_t chunks = (p.T + kTC - 1) / kTC;
+  int64_t r = chunks < kMaxRanges ? chunks : kMaxRanges;
+  const int64_t per = (chunks + r - 1) / r;
+  r = (chunks + per - 1) / per;
+  w.ranges = static_cast<int>(r);
+  w.range_chunks = static_cast<int>(per);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t hc = static_cast<size_t>(p.hidden) * p.C * sizeof(float);
+  const size_t h = static_cast<size_t>(p.hidden) * sizeof(float);
+  w.ma = 0;
+  w.mb = up(w.ma + r * hc);
+  w.mo = up(w.mb + r * hc);
+  w.sa = up(w.mo + r * hc);
+  w.sb = up(w.sa + r * h);
+  w.tg = up(w.sb + r * h);
+  w.tb = up(w.tg + hc);
+  w.total = up(w.tb + hc);
+  return w;
+}
+
+template <typename K>
+hipError_t grid_for(K kern, size_t lds, int want, int* grid) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 0, per_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds)) != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  *grid = want < cus * per_cu ? want : cus * per_cu;
+  return hipSuccess;
+}
+
+template <int KS>
+hipError_t launch_bwd(const TransProblem& p, const TransBwdArgs& a, char* ws, hipStream_t s) {
+  const TWs w = tws(p);
+  hipError_t e;
+  {
+    const size_t lds = TransLayout<KS>::lds_bytes();
+    int grid = 0;
+    if ((e = grid_for(transition_bwd_dx<KS>, lds, (p.tiles + kWaves - 1) / kWaves, &grid)) != hipSuccess) return e;
+    KernelTimer timer("transition_bwd_dx", s);
+    hipLaunchKernelGGL(transition_bwd_dx<KS>, dim3(grid), dim3(kThreads), lds, s, p, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    const size_t lds = WLayout<KS>::bytes();
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(transition_bwd_wpart<KS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    const int ngroups = p.hidden / kHC;
+    KernelTimer timer("transition_bwd_wpart", s);
+    hipLaunchKernelGGL(transition_bwd_wpart<KS>, dim3(ngroups * w.ranges), dim3(kThreads), lds, s, p, a, ngroups,
+                       w.ranges, w.range_chunks, reinterpret_cast<float*>(ws + w.ma),
+                       reinterpret_cast<float*>(ws + w.mb), reinterpret_cast<float*>(ws + w.mo),
+                       reinterpret_cast<float*>(ws + w.sa), reinterpret_cast<float*>(ws + w.sb));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  KernelTimer timer("transition_bwd_finalize", s);
+  hipLaunchKernelGGL(transition_fin_hidden, dim3(p.hidden), dim3(kFinThreads), 0, s, p, a, w.ranges,
+                     reinterpret_cast<const float*>(ws + w.ma), reinterpret_cast<const float*>(ws + w.mb),
+                     reinterpret_cast<const float*>(ws + w.sa), reinterpret_cast<const float*>(ws + w.sb),
+                     reinterpret_cast<float*>(ws + w.tg), reinterpret_cast<float*>(ws + w.tb));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(transition_fin_out, dim3(p.C), dim3(kFinThreads), 0, s, p, a, w.ranges,
+                     reinterpret_cast<const float*>(ws + w.mo));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(transition_fin_cols, dim3(p.C), dim3(kFinThreads), 0, s, p, a,
+                     reinterpret_cast<const float*>(ws + w.tg), reinterpret_cast<const float*>(ws + w.tb));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t transition_bwd_workspace_bytes(const TransProblem& p) { return tws(p).total; }
+
+hipError_t launch_transition_bwd(const TransProblem& p, const TransBwdArgs& a, void* ws, hipStream_t s) {
+  if (p.C == 128) return launch_bwd<8>(p, a, static_cast<char*>(ws), s);
+  if (p.C == 64) return launch_bwd<4>(p, a, static_cast<char*>(ws), s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace evo

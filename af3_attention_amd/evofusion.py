@@ -155,3 +155,64 @@ def transition_fwd(x, gamma, beta, w_a, w_b, w_out, *, eps: float = 1e-5, need_s
                                     _ptr(out["mean"]), _ptr(out["rstd"]), _stream(dev))
     _lib.check(st, "evoattn_transition_fwd")
     return out
+
+
+def transition_bwd_workspace_bytes(a, b, channels, expansion, dtype=torch.bfloat16) -> int:
+    return int(_lib.load().evoattn_transition_bwd_workspace_bytes(a, b, channels, expansion, _DTYPES[dtype]))
+
+
+def transition_bwd(x, gamma, beta, w_a, w_b, w_out, mean, rstd, dout, *, workspace=None):
+    """Gradients of sum(out * dout): dict dx (x's dtype), dgamma, dbeta (fp32 [C]),
+    dw_a, dw_b (fp32 [n*C, C]), dw_out (fp32 [C, n*C])."""
+    lib = _lib.load()
+    A, B, C = x.shape
+    dev = x.device
+    hidden = w_a.shape[0]
+    _check(x, "x", x.shape, x.dtype, dev)
+    _check(gamma, "gamma", (C,), torch.float32, dev)
+    _check(beta, "beta", (C,), torch.float32, dev)
+    _check(w_a, "w_a", (hidden, C), x.dtype, dev)
+    _check(w_b, "w_b", (hidden, C), x.dtype, dev)
+    _check(w_out, "w_out", (C, hidden), x.dtype, dev)
+    _check(mean, "mean", (A * B,), torch.float32, dev)
+    _check(rstd, "rstd", (A * B,), torch.float32, dev)
+    _check(dout, "dout", x.shape, x.dtype, dev)
+    out = {"dx": torch.empty_like(x), "dgamma": torch.empty(C, dtype=torch.float32, device=dev),
+           "dbeta": torch.empty(C, dtype=torch.float32, device=dev),
+           "dw_a": torch.empty((hidden, C), dtype=torch.float32, device=dev),
+           "dw_b": torch.empty((hidden, C), dtype=torch.float32, device=dev),
+           "dw_out": torch.empty((C, hidden), dtype=torch.float32, device=dev)}
+    n = hidden // C
+    ws_bytes = transition_bwd_workspace_bytes(A, B, C, n, x.dtype)
+    ws = workspace
+    if ws is None or ws.numel() < ws_bytes:
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = lib.evoattn_transition_bwd(A, B, C, n, _DTYPES[x.dtype], _ptr(x), _ptr(gamma), _ptr(beta), _ptr(w_a),
+                                    _ptr(w_b), _ptr(w_out), _ptr(mean), _ptr(rstd), _ptr(dout), _ptr(out["dx"]),
+                                    _ptr(out["dgamma"]), _ptr(out["dbeta"]), _ptr(out["dw_a"]), _ptr(out["dw_b"]),
+                                    _ptr(out["dw_out"]), _ptr(ws), ws_bytes, _stream(dev))
+    _lib.check(st, "evoattn_transition_bwd")
+    return out
+
+
+class TransitionFunction(torch.autograd.Function):
+    """Differentiable fused SwiGLU transition."""
+
+    @staticmethod
+    def forward(ctx, x, gamma, beta, w_a, w_b, w_out, eps):
+        x = x.contiguous()
+        r = transition_fwd(x, gamma, beta, w_a, w_b, w_out, eps=eps)
+        ctx.save_for_backward(x, gamma, beta, w_a, w_b, w_out, r["mean"], r["rstd"])
+        return r["out"]
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, gamma, beta, w_a, w_b, w_out, mean, rstd = ctx.saved_tensors
+        g = transition_bwd(x, gamma, beta, w_a, w_b, w_out, mean, rstd, dout.contiguous())
+        return (g["dx"], g["dgamma"], g["dbeta"], g["dw_a"].to(w_a.dtype), g["dw_b"].to(w_b.dtype),
+                g["dw_out"].to(w_out.dtype), None)
+
+
+def transition(x, gamma, beta, w_a, w_b, w_out, *, eps: float = 1e-5):
+    """Differentiable fused SwiGLU transition: out = (silu(y w_a^T) * y w_b^T) w_out^T, y = LN(x)."""
+    return TransitionFunction.apply(x, gamma, beta, w_a, w_b, w_out, float(eps))

@@ -118,6 +118,26 @@ evoattn_status_t evoattn_transition_fwd(int64_t a, int64_t b, int64_t channels, 
                                         const void* w_a, const void* w_b, const void* w_out, void* out,
                                         float* mean, float* rstd, void* stream);
 
+/* Bytes of workspace evoattn_transition_bwd needs (fixed-order partial sums of the
+ * weight gradients over at most 32 token ranges: O(ranges * n*C * C)).  Returns
+ * 0 and records an error detail if the problem is invalid or unsupported. */
+size_t evoattn_transition_bwd_workspace_bytes(int64_t a, int64_t b, int64_t channels, int64_t expansion,
+                                              int dtype);
+
+/* Backward of L = sum out * dout through evoattn_transition_fwd.  Inputs: the
+ * forward's inputs, its mean and rstd (required), dout (bf16, layout of x).
+ * Outputs: dx (bf16), dgamma, dbeta (fp32 [C]), dw_a, dw_b (fp32 [n*C, C]),
+ * dw_out (fp32 [C, n*C]).  a, b and h are recomputed on chip, never stored; the
+ * sums over tokens run in a fixed order (bit-identical across calls).  da, db,
+ * h, y and xhat are rounded to bf16 as matrix-core operands; sums are fp32. */
+evoattn_status_t evoattn_transition_bwd(int64_t a, int64_t b, int64_t channels, int64_t expansion, int dtype,
+                                        const void* x, const float* gamma, const float* beta,
+                                        const void* w_a, const void* w_b, const void* w_out,
+                                        const float* mean, const float* rstd, const void* dout,
+                                        void* dx, float* dgamma, float* dbeta,
+                                        float* dw_a, float* dw_b, float* dw_out,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -122,3 +122,93 @@ def test_fwd_unsupported_shapes_fail_loudly():
     g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in f.items()}
     with pytest.raises(ea.EvoAttnError, match="bf16"):
         ea.transition_fwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"])
+
+
+# ================================================================ backward
+#
+# Every matrix-core operand of the backward (y, xhat, dout, da, db, h) is bf16,
+# i.e. rounded by at most 2^-8 of itself, and each result sums n*C or T such
+# terms in fp32.  Independent roundings give each gradient a relative error of
+# a few tenths of a percent of its max norm (the forward's is 0.3-0.5 %); dx also
+# carries its own final rounding.  The test requires max|err| <= 2e-2 max|ref|
+# for dx and every weight gradient, and bit-identical results from two calls.
+
+BWD_REL = 2e-2
+
+
+def gpu_bwd(inp, reps=2):
+    import af3_attention_amd as ea
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    fw = ea.transition_fwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"], eps=inp["eps"])
+    outs = [ea.transition_bwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"], fw["mean"],
+                              fw["rstd"], g["dout"]) for _ in range(reps)]
+    torch.cuda.synchronize()
+    return outs
+
+
+def check_bwd(inp, ia=None, ib=None):
+    got, again = gpu_bwd(inp)
+    for n in got:
+        assert torch.equal(got[n], again[n]), f"{n}: two calls differ"
+        assert bool(torch.isfinite(got[n]).all()), f"{n}: non-finite"
+    sub = inp
+    dx = got["dx"]
+    if ia is not None:
+        keep = torch.zeros(inp["x"].shape[:2], dtype=torch.bool)
+        keep[ia[:, None], ib[None, :]] = True
+        assert bool((dx.cpu()[~keep] == 0).all()), "dx must vanish where dout is zero"
+        dx = dx[ia][:, ib]
+        sub = dict(inp)
+        sub["x"] = inp["x"][ia][:, ib]
+        sub["dout"] = inp["dout"][ia][:, ib]
+    ref = oracle.transition_bwd(f64(sub["x"]), f64(sub["gamma"]), f64(sub["beta"]), sub["eps"], f64(sub["w_a"]),
+                                f64(sub["w_b"]), f64(sub["w_out"]), f64(sub["dout"]))
+    errs = {}
+    for n in ("dx", "dgamma", "dbeta", "dw_a", "dw_b", "dw_out"):
+        g = f64(dx) if n == "dx" else f64(got[n])
+        e = float(np.abs(g - ref[n]).max() / np.abs(ref[n]).max())
+        errs[n] = e
+    print("bwd", errs, flush=True)
+    for n, e in errs.items():
+        assert e <= BWD_REL, f"{n}: max err / max|ref| = {e:.2e}"
+
+
+@pytest.mark.parametrize("A,B,C,n", [(16, 16, 128, 4), (7, 9, 128, 4), (33, 20, 64, 4), (5, 5, 128, 1),
+                                     (12, 11, 64, 2), (1, 1, 128, 4), (40, 41, 128, 4), (70, 70, 64, 4)])
+def test_bwd_shapes(A, B, C, n):
+    banner(f"bwd A={A} B={B} C={C} n={n}")
+    check_bwd(generate_transition(A, B, C, n, dtype=torch.bfloat16, seed=A * 7 + n))
+
+
+@pytest.mark.parametrize("name", ["pair_transition_bf16_n384", "msa_transition_bf16_s512_n384"])
+def test_bwd_workloads_sampled(name):
+    """Full sizes in the benchmark's launch configuration with dout zero outside a
+    40 x 40 token sub-grid: the weight gradients then equal the sub-grid's
+    exactly, dx matches on it and vanishes elsewhere."""
+    w = TRANSITION_WORKLOADS[name]
+    banner("bwd " + name)
+    inp = generate_transition_workload(w)
+    ia, ib = sample_axis(w.a, 40, 3), sample_axis(w.b, 40, 4)
+    keep = torch.zeros((w.a, w.b), dtype=torch.bool)
+    keep[ia[:, None], ib[None, :]] = True
+    inp["dout"] = inp["dout"] * keep[:, :, None].to(inp["dout"].dtype)
+    check_bwd(inp, ia, ib)
+
+
+def test_autograd_matches_entry_points():
+    import af3_attention_amd as ea
+    banner("transition autograd")
+    inp = generate_transition(20, 24, 128, 4, dtype=torch.bfloat16, seed=11)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    leaves = {n: g[n].clone().requires_grad_(True) for n in ("x", "gamma", "beta", "w_a", "w_b", "w_out")}
+    out = ea.transition(leaves["x"], leaves["gamma"], leaves["beta"], leaves["w_a"], leaves["w_b"], leaves["w_out"])
+    (out.float() * g["dout"].float()).sum().backward()
+    fw = ea.transition_fwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"])
+    ref = ea.transition_bwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"], fw["mean"], fw["rstd"],
+                            g["dout"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, fw["out"])
+    assert torch.equal(leaves["x"].grad, ref["dx"])
+    assert torch.equal(leaves["gamma"].grad, ref["dgamma"]) and torch.equal(leaves["beta"].grad, ref["dbeta"])
+    for n in ("w_a", "w_b", "w_out"):
+        assert torch.equal(leaves[n].grad, ref["d" + n].to(torch.bfloat16)), n

@@ -44,7 +44,8 @@ using proj::hi_bf16;
 using proj::lo_bf16;
 
 constexpr int kTC = 64;          // tokens per staged chunk of the partial-sum kernel
-constexpr int kMaxRanges = 32;   // token ranges of the partial sums
+constexpr int kMaxRanges = 64;   // token ranges of the partial sums (at most)
+constexpr int kTargetBlocks = 256;  // one partial-sum workgroup per CU
 constexpr int kFinThreads = 256;
 
 __device__ __forceinline__ float sigmoid_f(float a) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-a * kLog2e)); }
@@ -587,8 +588,12 @@ struct TWs {
 
 TWs tws(const TransProblem& p) {
   TWs w{};
+  // Enough ranges that (hidden groups x ranges) fills the CUs once.
   const int64_t chunks = (p.T + kTC - 1) / kTC;
-  int64_t r = chunks < kMaxRanges ? chunks : kMaxRanges;
+  const int64_t groups = p.hidden / kHC;
+  int64_t r = (kTargetBlocks + groups - 1) / groups;
+  r = r < kMaxRanges ? r : kMaxRanges;
+  r = r < chunks ? r : chunks;
   const int64_t per = (chunks + r - 1) / r;
   r = (chunks + per - 1) / per;
   w.ranges = static_cast<int>(r);

@@ -65,6 +65,9 @@ KERNEL_SOURCES = {
     "ln_proj_fwd": ["kernels_ln_proj.hip", "proj_common.h"],
     "ln_proj_bwd_dx": ["kernels_ln_proj_bwd.hip", "proj_common.h"],
     "ln_proj_bwd_mpart": ["kernels_ln_proj_bwd.hip", "proj_common.h"],
+    "transition_fwd": ["kernels_transition.hip", "transition_common.h", "proj_common.h"],
+    "transition_bwd_dx": ["kernels_transition_bwd.hip", "transition_common.h", "proj_common.h"],
+    "transition_bwd_wpart": ["kernels_transition_bwd.hip", "transition_common.h", "proj_common.h"],
 }
 
 
@@ -110,9 +113,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first (the GPU clocks take some tens of ms to settle)")
     ap.add_argument("--workload", default="tri_start_bf16_n384",
-                    help="an attention workload, or a layer norm + projection workload "
-                         "(pair_proj_bf16_n384, pair_proj_end_bf16_n768, msa_proj_bf16_s512_n384): "
-                         "the latter prints the projection step's own line")
+                    help="an attention workload, a layer norm + projection workload "
+                         "(pair_proj_bf16_n384, pair_proj_end_bf16_n768, msa_proj_bf16_s512_n384) or a SwiGLU "
+                         "transition workload (pair_transition_bf16_n384, msa_transition_bf16_s512_n384): the "
+                         "latter two print their step's own line")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -467,6 +471,171 @@ def proj_unfused(w, g, args, stream):
             "ops": "native_layer_norm, mm per projection, addmm, mm (weight grads), native_layer_norm_backward"}
 
 
+# ---------------------------------------------------------------- SwiGLU transition
+
+TRANS_METRIC = "SwiGLU transition fwd+bwd TFLOP/s (9 T*C*nC products, recompute not counted)"
+
+# Products of shape T x C x nC each kernel launch performs (its own algorithm,
+# recomputation included), times 2 flops.
+TRANS_KERNEL_PRODUCTS = {"transition_fwd": 3, "transition_bwd_dx": 5, "transition_bwd_wpart": 6}
+
+
+def transition_cpu_baseline(w, inp, target_s):
+    """The fp64 oracle (fwd + bwd) on an s x s token sub-grid sized to ~target_s seconds."""
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    f = lambda t: t.detach().cpu().double().numpy()
+    wts = [f(inp[n]) for n in ("gamma", "beta")] + [inp["eps"]] + [f(inp[n]) for n in ("w_a", "w_b", "w_out")]
+
+    def run(s):
+        x, do = f(inp["x"][:s, :s]), f(inp["dout"][:s, :s])
+        t0 = time.perf_counter()
+        oracle.transition_fwd(x, *wts)
+        oracle.transition_bwd(x, *wts, do)
+        return time.perf_counter() - t0
+
+    side = min(w.a, w.b)
+    s, secs = 8, run(8)
+    for _ in range(3):
+        if secs >= 0.6 * target_s or s >= side:
+            break
+        s = int(min(side, max(s + 1, s * (target_s / max(secs, 1e-6)) ** 0.5)))
+        secs = run(s)
+    reps = 1
+    if s >= side and secs < 0.6 * target_s:
+        reps = int(min(60, max(2, round(target_s / max(secs, 1e-6)))))
+        secs = sum(run(s) for _ in range(reps))
+    flops = 2.0 * 9 * s * s * w.channels * w.hidden * reps
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{s} x {s} token sub-grid of {w.name} (fwd+bwd, fp64)"
+                      + (f" x {reps} passes" if reps > 1 else "") + f", {secs:.2f} s", "seconds": secs}
+
+
+def transition_unfused(w, g, args, stream):
+    """The same step as separate torch kernels in bf16 (layer norm, one mm per
+    product, elementwise gate and its derivative, layer-norm backward), which
+    materialise y, a, b, h and their gradients in HBM.  Only 2-D products."""
+    import torch
+
+    T, C, Hd = w.tokens, w.channels, w.hidden
+    dt = w.torch_dtype
+    dev = g["x"].device
+    x2, do2 = g["x"].view(T, C), g["dout"].view(T, C)
+    gam, bet = g["gamma"].to(dt), g["beta"].to(dt)
+    wa, wb, wo = g["w_a"], g["w_b"], g["w_out"]
+    wat, wbt, wot = wa.t().contiguous(), wb.t().contiguous(), wo.t().contiguous()
+
+    def step():
+        y, mean, rstd = torch.native_layer_norm(x2, (C,), gam, bet, g["eps"])
+        a = torch.mm(y, wat)
+        b = torch.mm(y, wbt)
+        sa = torch.nn.functional.silu(a)
+        h = sa * b
+        torch.mm(h, wot)
+        dh = torch.mm(do2, wo)
+        sg = torch.sigmoid(a)
+        da = dh * b * (sg * (1 + a * (1 - sg)))
+        db = dh * sa
+        dy = torch.mm(da, wa)
+        dy.addmm_(db, wb)
+        torch.mm(do2.t(), h)
+        torch.mm(da.t(), y)
+        torch.mm(db.t(), y)
+        torch.ops.aten.native_layer_norm_backward(dy, x2, (C,), mean, rstd, gam, bet, [True, True, True])
+
+    for _ in range(max(5, args.warmup // 10)):
+        step()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    return {"ms_per_step": ms, "tflops": 2.0 * 9 * T * C * Hd / (ms * 1e-3) / 1e12,
+            "peak_hbm_extra_bytes": int(torch.cuda.max_memory_allocated(dev) - base),
+            "ops": "native_layer_norm, mm per product, silu/sigmoid elementwise, native_layer_norm_backward"}
+
+
+def transition_main(args, w):
+    import torch
+    import af3_attention_amd as ea
+    from af3_attention_amd import _lib
+    from workloads import generate_transition_workload
+
+    dev = torch.device("cuda:0")
+    inp_cpu = generate_transition_workload(w, seed=args.seed)
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp_cpu.items()}
+    ws = torch.empty(ea.transition_bwd_workspace_bytes(w.a, w.b, w.channels, w.expansion), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        fw = ea.transition_fwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"], eps=g["eps"])
+        ea.transition_bwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"], fw["mean"], fw["rstd"],
+                          g["dout"], workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, kernel_timing=False):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        _lib.timing_collect()
+        _lib.timing_enable(kernel_timing)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        _lib.timing_enable(False)
+        return start.elapsed_time(stop) / args.steps, _lib.timing_collect()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    base_mem = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ms, _ = timed(step)
+    peak_fused = torch.cuda.max_memory_allocated(dev) - base_mem
+    kernels = {}
+    if not args.no_kernel_timing:
+        _, kernels = timed(step, True)
+    unit_flops = 2.0 * w.tokens * w.channels * w.hidden
+    value = 9 * unit_flops / (ms * 1e-3) / 1e12
+    roofline = None
+    if kernels:
+        name, (count, tot) = max(kernels.items(), key=lambda kv: kv[1][1])
+        avg_ms = tot / count
+        if name in TRANS_KERNEL_PRODUCTS:
+            achieved = TRANS_KERNEL_PRODUCTS[name] * unit_flops / (avg_ms * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_BF16_MFMA_TFLOPS, "traffic": recorded_traffic(name, w.name),
+                        "kernel": name, "avg_launch_ms": avg_ms, "launches": count,
+                        "algorithmic_flops": TRANS_KERNEL_PRODUCTS[name] * unit_flops}
+    unfused = None if args.no_unfused else transition_unfused(w, g, args, stream)
+    cpu = None if args.no_cpu_baseline else transition_cpu_baseline(w, inp_cpu, args.cpu_seconds)
+    line = {
+        "metric": TRANS_METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "a": w.a, "b": w.b, "channels": w.channels, "expansion": w.expansion,
+                   "seed": args.seed},
+        "frac_of_bf16_peak": value / PEAK_BF16_MFMA_TFLOPS,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "unfused_torch": unfused,
+        "kernels_ms_per_step": {k: tot / args.steps for k, (c, tot) in kernels.items()},
+        "peak_hbm_extra_bytes": int(peak_fused),
+    }
+    if args.copy_calibration:
+        line["copy_calibration"] = copy_calibration(dev)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.memory_curve and args.gpus == 1:
@@ -477,9 +646,12 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
-    from workloads import PROJ_WORKLOADS
+    from workloads import PROJ_WORKLOADS, TRANSITION_WORKLOADS
     if args.workload in PROJ_WORKLOADS:
         proj_main(args, PROJ_WORKLOADS[args.workload])
+        return
+    if args.workload in TRANSITION_WORKLOADS:
+        transition_main(args, TRANSITION_WORKLOADS[args.workload])
         return
 
     import torch

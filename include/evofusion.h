@@ -119,7 +119,7 @@ evoattn_status_t evoattn_transition_fwd(int64_t a, int64_t b, int64_t channels, 
                                         float* mean, float* rstd, void* stream);
 
 /* Bytes of workspace evoattn_transition_bwd needs (fixed-order partial sums of the
- * weight gradients over at most 32 token ranges: O(ranges * n*C * C)).  Returns
+ * weight gradients over at most 64 token ranges: O(ranges * n*C * C)).  Returns
  * 0 and records an error detail if the problem is invalid or unsupported. */
 size_t evoattn_transition_bwd_workspace_bytes(int64_t a, int64_t b, int64_t channels, int64_t expansion,
                                               int dtype);

@@ -262,3 +262,72 @@ def test_ln_proj_bwd_workspace_query():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful where no GPU is present")
 def test_ln_proj_bwd_valid_call_without_device_reports_device_error():
     assert proj_bwd() == DEVICE
+
+
+def trans_fwd(**kw):
+    lib = _lib.load()
+    args = dict(a=8, b=8, c=128, n=4, dtype=1, eps=1e-5, x=A, gamma=A, beta=A, wa=A, wb=A, wo=A, out=A, mean=A, rstd=A)
+    args.update(kw)
+    return lib.evoattn_transition_fwd(*(args[k] for k in ("a", "b", "c", "n", "dtype", "eps", "x", "gamma", "beta",
+                                                          "wa", "wb", "wo", "out", "mean", "rstd")), None)
+
+
+def trans_bwd(**kw):
+    lib = _lib.load()
+    args = dict(a=8, b=8, c=64, n=4, dtype=1, x=A, gamma=A, beta=A, wa=A, wb=A, wo=A, mean=A, rstd=A, dout=A, dx=A,
+                dgamma=A, dbeta=A, dwa=A, dwb=A, dwo=A, ws=A, ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.evoattn_transition_bwd(*(args[k] for k in (
+        "a", "b", "c", "n", "dtype", "x", "gamma", "beta", "wa", "wb", "wo", "mean", "rstd", "dout", "dx", "dgamma",
+        "dbeta", "dwa", "dwb", "dwo", "ws", "ws_bytes")), None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(a=0), INVALID, "sizes"),
+    (dict(n=0), INVALID, "sizes"),
+    (dict(dtype=5), INVALID, "dtype"),
+    (dict(eps=-1.0), INVALID, "eps"),
+    (dict(dtype=0), UNSUPPORTED, "bf16"),
+    (dict(c=96), UNSUPPORTED, "channels"),
+    (dict(n=17), UNSUPPORTED, "expansion"),
+    (dict(a=1 << 14, b=1 << 14), UNSUPPORTED, "too large"),
+    (dict(x=None), INVALID, "x must not be NULL"),
+    (dict(wo=None), INVALID, "w_out must not be NULL"),
+    (dict(wa=A + 4), INVALID, "aligned"),
+    (dict(out=None), INVALID, "out must not be NULL"),
+    (dict(mean=None), INVALID, "both"),
+])
+def test_transition_fwd_validation(kw, code, needle):
+    assert trans_fwd(**kw) == code
+    assert needle in detail()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(c=32), UNSUPPORTED, "channels"),
+    (dict(mean=None), INVALID, "mean must not be NULL"),
+    (dict(dout=None), INVALID, "dout must not be NULL"),
+    (dict(dx=A + 2), INVALID, "aligned"),
+    (dict(dwo=None), INVALID, "dw_out must not be NULL"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(ws_bytes=64), WORKSPACE, "workspace"),
+    (dict(ws=A + 64), INVALID, "256-byte"),
+])
+def test_transition_bwd_validation(kw, code, needle):
+    assert trans_bwd(**kw) == code
+    assert needle in detail()
+
+
+def test_transition_workspace_query():
+    lib = _lib.load()
+    n = lib.evoattn_transition_bwd_workspace_bytes(384, 384, 128, 4, 1)
+    assert n % 256 == 0
+    # partial sums over at most 64 ranges of three n*C x C arrays, two n*C vectors, two n*C x C products
+    hc = 512 * 128 * 4
+    assert n <= 64 * (3 * hc + 2 * 512 * 4) + 2 * hc + 8 * 256
+    assert lib.evoattn_transition_bwd_workspace_bytes(384, 384, 128, 4, 0) == 0   # fp32: unsupported
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful where no GPU is present")
+def test_transition_valid_call_without_device_reports_device_error():
+    assert trans_fwd() == DEVICE
+    assert trans_bwd() == DEVICE

@@ -536,33 +536,48 @@ __global__ __launch_bounds__(kVecThreads) void bwd_mpart_vector(ProjProblem p, P
 // ---------------------------------------------------------------- 3. finalize
 
 // One workgroup per output row o: M and s from the partials, dW, and the
-// per-(o, c) products whose sums over o are dgamma and dbeta.  Each of the four
-// wave slots sums every fourth range (in increasing order) for 64 channels; the
-// four partial sums are then added in slot order.
+// per-(o, c) products whose sums over o are dgamma and dbeta.  1024 threads = 8
+// slots x 128 channels: slot k sums ranges k, k + 8, ... in increasing order (all
+// its loads in flight at once), then the 8 slot sums are added in slot order.
+constexpr int kFinSlots = 8;
+constexpr int kFinCols = 128;
+constexpr int kFinRowThreads = kFinSlots * kFinCols;
+
 template <typename T>
-__global__ __launch_bounds__(kVecThreads) void bwd_finalize_rows(ProjProblem p, ProjBwdArgs a, int ranges,
-                                                                 const float* mpart, const float* spart,
-                                                                 float* tgamma, float* tbeta) {
-  __shared__ float part[kVecThreads];
+__global__ __launch_bounds__(kFinRowThreads) void bwd_finalize_rows(ProjProblem p, ProjBwdArgs a, int ranges,
+                                                                   const float* mpart, const float* spart,
+                                                                   float* tgamma, float* tbeta) {
+  __shared__ float part[kFinSlots][kFinCols];
+  __shared__ float s_r[kFinRowThreads];
+  __shared__ float s_sh;
   const int o = blockIdx.x;
   const int po = padded_outputs(p);
-  const int slot = threadIdx.x >> 6;
-  const int cl = threadIdx.x & 63;
-  float s = 0.f;
-  for (int r = 0; r < ranges; ++r) s += spart[static_cast<int64_t>(r) * po + o];
-  for (int c0 = 0; c0 < p.C; c0 += 64) {
+  const int slot = threadIdx.x / kFinCols;
+  const int cl = threadIdx.x - slot * kFinCols;
+  // s: every range's partial loaded at once, then summed in increasing range order.
+  for (int r = threadIdx.x; r < ranges; r += kFinRowThreads) s_r[r] = spart[static_cast<int64_t>(r) * po + o];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+    for (int r = 0; r < ranges; ++r) s += s_r[r];
+    s_sh = s;
+  }
+  for (int c0 = 0; c0 < p.C; c0 += kFinCols) {
     const int c = c0 + cl;
     float m = 0.f;
     if (c < p.C) {
       const float* src = mpart + static_cast<int64_t>(o) * p.C + c;
       const int64_t rstride = static_cast<int64_t>(po) * p.C;
-#pragma unroll 4
-      for (int r = slot; r < ranges; r += 4) m += src[r * rstride];
+#pragma unroll 8
+      for (int r = slot; r < ranges; r += kFinSlots) m += src[r * rstride];
     }
-    part[threadIdx.x] = m;
+    part[slot][cl] = m;
     __syncthreads();
     if (slot == 0 && c < p.C) {
-      m = ((part[cl] + part[64 + cl]) + part[128 + cl]) + part[192 + cl];
+      m = part[0][cl];
+#pragma unroll
+      for (int k = 1; k < kFinSlots; ++k) m += part[k][cl];
+      const float s = s_sh;
       const float dw = fmaf(m, a.gamma[c], s * a.beta[c]);
       if (o < p.n_qkv)
         a.dw_qkv[static_cast<int64_t>(o) * p.C + c] = dw;
@@ -741,11 +756,11 @@ hipError_t launch_ln_proj_bwd(const ProjProblem& p, const ProjBwdArgs& a, void* 
   {
     KernelTimer timer("ln_proj_bwd_finalize", s);
     if (p.dtype == 1)
-      hipLaunchKernelGGL(bwd_finalize_rows<uint16_t>, dim3(p.n_out), dim3(kVecThreads), 0, s, p, a, w.ranges, mpart,
-                         spart, tgamma, tbeta);
+      hipLaunchKernelGGL(bwd_finalize_rows<uint16_t>, dim3(p.n_out), dim3(kFinRowThreads), 0, s, p, a, w.ranges,
+                         mpart, spart, tgamma, tbeta);
     else
-      hipLaunchKernelGGL(bwd_finalize_rows<float>, dim3(p.n_out), dim3(kVecThreads), 0, s, p, a, w.ranges, mpart,
-                         spart, tgamma, tbeta);
+      hipLaunchKernelGGL(bwd_finalize_rows<float>, dim3(p.n_out), dim3(kFinRowThreads), 0, s, p, a, w.ranges,
+                         mpart, spart, tgamma, tbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_finalize_cols, dim3(p.C), dim3(kVecThreads), 0, s, p, a, tgamma, tbeta);
   }

@@ -20,7 +20,7 @@
 //      operands whose contraction index is the token; they are exchanged through
 //      LDS and accumulated into M_a, M_b and dout^T h against xhat and dout staged
 //      per 64 tokens.  The hidden groups of one range share an XCD.
-//   3. Finalize: partials summed in increasing range order (fixed slots), dw_a,
+//   3. Finalize: partials summed in fixed slots of ranges (each in increasing order), dw_a,
 //      dw_b, dw_out, and dgamma / dbeta by fixed-shape sums.
 // Nothing of size tokens x hidden is written to memory; every sum has a fixed order.
 
@@ -499,37 +499,58 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
 
 __device__ __forceinline__ float bf(const void* p, int64_t i) { return bf16_to_f32(static_cast<const uint16_t*>(p)[i]); }
 
-// One workgroup per hidden unit j: M_a, M_b, s_a, s_b over the ranges (four fixed
-// slots, then in slot order), dw_a, dw_b, and the products whose sums over j are
-// dgamma and dbeta.
-__global__ __launch_bounds__(kFinThreads) void transition_fin_hidden(TransProblem p, TransBwdArgs a, int ranges,
+// 1024 threads = 8 slots x 128 columns: slot k sums ranges k, k + 8, ... in
+// increasing order (its loads all in flight), then the slot sums are added in
+// slot order.
+constexpr int kSlots = 8;
+constexpr int kCols = 128;
+constexpr int kRowThreads = kSlots * kCols;
+
+// One workgroup per hidden unit j: M_a, M_b, s_a, s_b over the ranges, dw_a, dw_b,
+// and the products whose sums over j are dgamma and dbeta.
+__global__ __launch_bounds__(kRowThreads) void transition_fin_hidden(TransProblem p, TransBwdArgs a, int ranges,
                                                                     const float* ma, const float* mb, const float* sa,
                                                                     const float* sb, float* tg, float* tb) {
-  __shared__ float part[2][kFinThreads];
+  __shared__ float part[2][kSlots][kCols];
+  __shared__ float s_r[2][kRowThreads / 2];
+  __shared__ float s_sh[2];
   const int j = blockIdx.x;
-  const int slot = threadIdx.x >> 6, cl = threadIdx.x & 63;
-  float s_a = 0.f, s_b = 0.f;
-  for (int r = 0; r < ranges; ++r) {
-    s_a += sa[static_cast<int64_t>(r) * p.hidden + j];
-    s_b += sb[static_cast<int64_t>(r) * p.hidden + j];
+  const int slot = threadIdx.x / kCols, cl = threadIdx.x - slot * kCols;
+  // s_a, s_b: every range's partial loaded at once, then summed in range order.
+  for (int r = threadIdx.x; r < 2 * ranges; r += kRowThreads) {
+    const int q = r / ranges, rr = r - q * ranges;
+    s_r[q][rr] = (q == 0 ? sa : sb)[static_cast<int64_t>(rr) * p.hidden + j];
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    float s = 0.f;
+    for (int r = 0; r < ranges; ++r) s += s_r[threadIdx.x][r];
+    s_sh[threadIdx.x] = s;
   }
   const int64_t rstride = static_cast<int64_t>(p.hidden) * p.C;
-  for (int c0 = 0; c0 < p.C; c0 += 64) {
+  for (int c0 = 0; c0 < p.C; c0 += kCols) {
     const int c = c0 + cl;
     float m_a = 0.f, m_b = 0.f;
     if (c < p.C) {
       const int64_t off = static_cast<int64_t>(j) * p.C + c;
-      for (int r = slot; r < ranges; r += 4) {
+#pragma unroll 8
+      for (int r = slot; r < ranges; r += kSlots) {
         m_a += ma[r * rstride + off];
         m_b += mb[r * rstride + off];
       }
     }
-    part[0][threadIdx.x] = m_a;
-    part[1][threadIdx.x] = m_b;
+    part[0][slot][cl] = m_a;
+    part[1][slot][cl] = m_b;
     __syncthreads();
     if (slot == 0 && c < p.C) {
-      m_a = ((part[0][cl] + part[0][64 + cl]) + part[0][128 + cl]) + part[0][192 + cl];
-      m_b = ((part[1][cl] + part[1][64 + cl]) + part[1][128 + cl]) + part[1][192 + cl];
+      m_a = part[0][0][cl];
+      m_b = part[1][0][cl];
+#pragma unroll
+      for (int k = 1; k < kSlots; ++k) {
+        m_a += part[0][k][cl];
+        m_b += part[1][k][cl];
+      }
+      const float s_a = s_sh[0], s_b = s_sh[1];
       const int64_t off = static_cast<int64_t>(j) * p.C + c;
       a.dw_a[off] = fmaf(m_a, a.gamma[c], s_a * a.beta[c]);
       a.dw_b[off] = fmaf(m_b, a.gamma[c], s_b * a.beta[c]);
@@ -541,14 +562,30 @@ __global__ __launch_bounds__(kFinThreads) void transition_fin_hidden(TransProble
   }
 }
 
-// One workgroup per channel c: dw_out[c][:] over the ranges in order.
-__global__ __launch_bounds__(kFinThreads) void transition_fin_out(TransProblem p, TransBwdArgs a, int ranges,
+// One workgroup per channel c: dw_out[c][:] over the ranges (the same slots).
+__global__ __launch_bounds__(kRowThreads) void transition_fin_out(TransProblem p, TransBwdArgs a, int ranges,
                                                                  const float* mo) {
+  __shared__ float part[kSlots][kCols];
   const int c = blockIdx.x;
-  for (int j = threadIdx.x; j < p.hidden; j += kFinThreads) {
+  const int slot = threadIdx.x / kCols, cl = threadIdx.x - slot * kCols;
+  const int64_t rstride = static_cast<int64_t>(p.C) * p.hidden;
+  for (int j0 = 0; j0 < p.hidden; j0 += kCols) {
+    const int j = j0 + cl;
     float s = 0.f;
-    for (int r = 0; r < ranges; ++r) s += mo[(static_cast<int64_t>(r) * p.C + c) * p.hidden + j];
-    a.dw_out[static_cast<int64_t>(c) * p.hidden + j] = s;
+    if (j < p.hidden) {
+      const float* src = mo + static_cast<int64_t>(c) * p.hidden + j;
+#pragma unroll 8
+      for (int r = slot; r < ranges; r += kSlots) s += src[r * rstride];
+    }
+    part[slot][cl] = s;
+    __syncthreads();
+    if (slot == 0 && j < p.hidden) {
+      s = part[0][cl];
+#pragma unroll
+      for (int k = 1; k < kSlots; ++k) s += part[k][cl];
+      a.dw_out[static_cast<int64_t>(c) * p.hidden + j] = s;
+    }
+    __syncthreads();
   }
 }
 
@@ -652,12 +689,12 @@ hipError_t launch_bwd(const TransProblem& p, const TransBwdArgs& a, char* ws, hi
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   KernelTimer timer("transition_bwd_finalize", s);
-  hipLaunchKernelGGL(transition_fin_hidden, dim3(p.hidden), dim3(kFinThreads), 0, s, p, a, w.ranges,
+  hipLaunchKernelGGL(transition_fin_hidden, dim3(p.hidden), dim3(kRowThreads), 0, s, p, a, w.ranges,
                      reinterpret_cast<const float*>(ws + w.ma), reinterpret_cast<const float*>(ws + w.mb),
                      reinterpret_cast<const float*>(ws + w.sa), reinterpret_cast<const float*>(ws + w.sb),
                      reinterpret_cast<float*>(ws + w.tg), reinterpret_cast<float*>(ws + w.tb));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(transition_fin_out, dim3(p.C), dim3(kFinThreads), 0, s, p, a, w.ranges,
+  hipLaunchKernelGGL(transition_fin_out, dim3(p.C), dim3(kRowThreads), 0, s, p, a, w.ranges,
                      reinterpret_cast<const float*>(ws + w.mo));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(transition_fin_cols, dim3(p.C), dim3(kFinThreads), 0, s, p, a,

@@ -12,7 +12,8 @@
 // bf16, C in {64, 128}.  A workgroup of 8 waves takes 256 tokens (one 32-token
 // tile per wave) at a time and streams the weights through LDS in chunks of 64
 // hidden units (w_a and w_b rows, the matching w_out columns), double-buffered:
-// every chunk is read once from L2 per 256 tokens.  Per chunk and 32 hidden
+// every chunk is read once from L2 per 256 tokens, copied straight from global
+// memory into LDS.  Per chunk and 32 hidden
 // units a wave forms a and b on the matrix cores (D[hidden][token]), applies
 // the gate in registers, and the packed accumulator registers are directly the
 // B operand of out += w_out[:, chunk] h (the A operand reads w_out with the same
@@ -52,20 +53,18 @@ __global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem 
   const int nch = p.hidden / kHC;
   const int npass = (p.tiles + kWaves - 1) / kWaves;
 
-  WeightChunks<KS> wch{static_cast<const uint16_t*>(a.w_a), static_cast<const uint16_t*>(a.w_b),
-                       static_cast<const uint16_t*>(a.w_out), p.hidden, tid};
-  auto load_w = [&](int ch) { wch.load(ch); };
-  auto store_w = [&](int buf) { wch.store(wbuf + buf * L::CHUNK); };
+  const int wave_u = pipe::wave_id();
+  const uint32_t wbuf_a = pipe::lds_addr(wbuf);
+  WeightCopy<KS> wc;
+  wc.init(a.w_a, a.w_b, a.w_out, p.hidden, wave_u, lane);
 
   for (int c = tid; c < C; c += kThreads) {
     s_gamma[c] = a.gamma[c];
     s_beta[c] = a.beta[c];
   }
   const int first = blockIdx.x;
-  if (first < npass) {
-    load_w(0);
-    store_w(0);
-  }
+  if (first < npass) wc.issue(0, wbuf_a, wave_u);
+  pipe::wait_vmcnt<0>();
   __syncthreads();
 
   const uint16_t* xg = static_cast<const uint16_t*>(a.x);
@@ -125,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem 
     for (int ch = 0; ch < nch; ++ch) {
       // The next chunk of weights (of this pass, or the first of the next pass).
       const bool more = ch + 1 < nch || pass + static_cast<int>(gridDim.x) < npass;
-      if (more) load_w(ch + 1 < nch ? ch + 1 : 0);
+      if (more) wc.issue(ch + 1 < nch ? ch + 1 : 0, wbuf_a + (buf ^ 1) * L::CHUNK, wave_u);
       const char* cw = wbuf + buf * L::CHUNK;
 #pragma unroll
       for (int ht = 0; ht < kHC / 32; ++ht) {
@@ -160,7 +159,9 @@ __global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem 
           }
         }
       }
-      if (more) store_w(buf ^ 1);
+      // This wave's copies of the next chunk have landed; the barrier publishes
+      // them and ends every wave's reads of this chunk.
+      pipe::wait_vmcnt<0>();
       __syncthreads();
       buf ^= 1;
     }

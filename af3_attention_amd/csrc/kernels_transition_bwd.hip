@@ -90,17 +90,16 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_dx(TransProblem p,
   const int npass = (p.tiles + kWaves - 1) / kWaves;
   const TrRead tr(lane);
 
-  WeightChunks<KS> wch{static_cast<const uint16_t*>(a.w_a), static_cast<const uint16_t*>(a.w_b),
-                       static_cast<const uint16_t*>(a.w_out), p.hidden, tid};
+  const int wave_u = pipe::wave_id();
+  WeightCopy<KS> wc;
+  wc.init(a.w_a, a.w_b, a.w_out, p.hidden, wave_u, lane);
   for (int c = tid; c < C; c += kThreads) {
     s_gamma[c] = a.gamma[c];
     s_beta[c] = a.beta[c];
   }
   const int first = blockIdx.x;
-  if (first < npass) {
-    wch.load(0);
-    wch.store(wbuf);
-  }
+  if (first < npass) wc.issue(0, wbuf_a, wave_u);
+  pipe::wait_vmcnt<0>();
   __syncthreads();
 
   const uint16_t* xg = static_cast<const uint16_t*>(a.x);
@@ -148,21 +147,14 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_dx(TransProblem p,
     for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x16{};
 
     for (int ch = 0; ch < nch; ++ch) {
-      // The next chunk is staged in two halves (one per 32 hidden units) to keep
-      // its registers few.
-      constexpr int NPH = (L::NP + 1) / 2;
+      // The next chunk (of this pass, or the first of the next) is copied into the
+      // other buffer while this one is used.
       const bool more = ch + 1 < nch || pass + static_cast<int>(gridDim.x) < npass;
-      const int next = ch + 1 < nch ? ch + 1 : 0;
-      char* nbuf = wbuf + (buf ^ 1) * L::CHUNK;
-      if (more) wch.template load<0, NPH>(next);
+      if (more) wc.issue(ch + 1 < nch ? ch + 1 : 0, wbuf_a + (buf ^ 1) * L::CHUNK, wave_u);
       const char* cw = wbuf + buf * L::CHUNK;
       const uint32_t cwa = wbuf_a + buf * L::CHUNK;
 #pragma unroll
       for (int ht = 0; ht < kHC / 32; ++ht) {
-        if (ht == 1 && more) {
-          wch.template store<0, NPH>(nbuf);
-          wch.template load<NPH, L::NP>(next);
-        }
         // a, b, dh: D[hidden][token] for 32 hidden units.
         const char* ra = cw + L::WA + (32 * ht + li) * L::PW + 16 * half;
         const char* rb = cw + L::WB + (32 * ht + li) * L::PW + 16 * half;
@@ -204,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_dx(TransProblem p,
             __builtin_amdgcn_sched_barrier(0);
           }
       }
-      if (more) wch.template store<NPH, L::NP>(nbuf);
+      pipe::wait_vmcnt<0>();
       __syncthreads();
       buf ^= 1;
     }

@@ -258,15 +258,27 @@ struct WLayout {
   using L = TransLayout<KS>;
   static constexpr int C = L::C;
   static constexpr int PX = 2 * C + 32;                 // staged token row (xhat or dout), bytes
-  static constexpr int STAGE = 2 * kTC * PX;            // xhat then dout
+  static constexpr int STAGE = 2 * kTC * PX;            // xhat then dout of one chunk
+  static constexpr int NSTAGE = 3;                      // chunks being read by C, read by A, written
   static constexpr int XCH = 4 * 3 * 2 * 64 * 16;       // exchange: job x (da, db, h) x k-step x lane
-  static constexpr int W0 = 8 * C;                      // weights (one chunk)
-  static constexpr int S0 = W0 + L::CHUNK;              // two stages
-  static constexpr int X0 = S0 + 2 * STAGE;             // exchange
-  static constexpr int SUMS = X0 + XCH;                 // 4 jobs x 2 x 32 floats
+  static constexpr int S0 = 0;
+  static constexpr int X0 = S0 + NSTAGE * STAGE;        // two exchange buffers
+  static constexpr int SUMS = X0 + 2 * XCH;             // 4 jobs x 2 x 32 floats
   static constexpr size_t bytes() { return static_cast<size_t>(SUMS) + 4 * 2 * 32 * 4; }
 };
 
+// One workgroup per (64-unit hidden group, token range); the range's tokens are
+// taken in chunks of 64 by two groups of waves, one chunk apart:
+//   waves 0..3 (phase A, chunk s + 1): job (32 hidden units ht, 32 tokens sub)
+//     forms a, b, dh as D[token][hidden] from the staged xhat and dout rows against
+//     weights held in registers, with gamma folded in: a = xhat (w_a diag(gamma))^T
+//     + w_a beta (and the same for b), then da, db, h, packed as operands whose
+//     contraction index is the token, go to an exchange buffer;
+//   waves 4..7 (phase C, chunk s): the product tiles M_a += da^T xhat,
+//     M_b += db^T xhat, Mo += dout^T h over the chunk's 64 tokens, then they stage
+//     chunk s + 2 (xhat normalised in registers, and dout), loaded one step
+//     earlier so that the loads overlap a barrier and a phase C.
+// Three stages and two exchange buffers: one barrier per step.
 template <int KS>
 __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem p, TransBwdArgs a, int ngroups,
                                                                    int ranges, int range_chunks, float* ma, float* mb,
@@ -277,122 +289,148 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
   constexpr int CT = C / 32;
   constexpr int PX = W::PX;
   constexpr int XPL = C / 8;                     // 16-byte pieces per token row
-  constexpr int NPC = kTC * XPL / kThreads;      // pieces of each tensor per thread
+  constexpr int CTHREADS = kThreads / 2;         // threads of the phase-C waves
+  constexpr int NPC = kTC * XPL / CTHREADS;      // pieces of each tensor per phase-C thread
   constexpr int NT = 3 * 2 * CT;                 // product tiles per workgroup
-  constexpr int TPW = (NT + kWaves - 1) / kWaves;
-  static_assert(kTC * XPL % kThreads == 0, "token pieces must divide evenly");
+  constexpr int TPW = NT / 4;                    // per phase-C wave
+  static_assert(kTC * XPL % CTHREADS == 0 && NT % 4 == 0, "work must divide evenly");
+  static_assert((2 * CT) % 4 == 0, "a phase-C wave's i-th tile has the same quantity for every wave");
   extern __shared__ __align__(16) char lds[];
-  float* s_gamma = reinterpret_cast<float*>(lds);
-  float* s_beta = s_gamma + C;
   const uint32_t base = lds_addr(lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = pipe::wave_id();
   const int half = lane >> 5;
   const int li = lane & 31;
   const TrRead tr(lane);
   const int blk = xcd_logical_block(blockIdx.x, ngroups * ranges);
   const int group = blk % ngroups;
   const int range = blk / ngroups;
+  const int h0 = group * kHC;
   const int64_t t_begin = static_cast<int64_t>(range) * range_chunks * kTC;
   const int64_t t_end = min(p.T, t_begin + static_cast<int64_t>(range_chunks) * kTC);
   const int nch = static_cast<int>((t_end - t_begin + kTC - 1) / kTC);
+  const bool is_a = wave < 4;
 
-  {
-    WeightChunks<KS> wch{static_cast<const uint16_t*>(a.w_a), static_cast<const uint16_t*>(a.w_b),
-                         static_cast<const uint16_t*>(a.w_out), p.hidden, tid};
-    wch.load(group);
-    wch.store(lds + W::W0);
-    for (int c = tid; c < C; c += kThreads) {
-      s_gamma[c] = a.gamma[c];
-      s_beta[c] = a.beta[c];
-    }
-  }
+  auto stage_x = [&](int c) { return base + W::S0 + (c % W::NSTAGE) * W::STAGE; };
+  // Exchange slot of (chunk parity, job, quantity 0 da / 1 db / 2 h, k-step) for one lane.
+  auto xslot = [&](int c, int job, int q, int kk) {
+    return W::X0 + (c & 1) * W::XCH + ((job * 3 + q) * 2 + kk) * 1024 + 16 * lane;
+  };
 
+  // ---- staging (phase-C waves): chunk c's xhat and dout rows, in registers then LDS
   const uint16_t* xg = static_cast<const uint16_t*>(a.x);
   const uint16_t* dog = static_cast<const uint16_t*>(a.dout);
+  const int ctid = tid - CTHREADS;
   u32x4 xr[NPC], dr[NPC];
   float xm[NPC], xs[NPC];
-  auto load = [&](int ch) {
-    const int64_t t0 = t_begin + static_cast<int64_t>(ch) * kTC;
+  // Tokens past the range are loaded from its last token (no branch around the
+  // loads) and staged as zeros.
+  // Addresses are a uniform base (the chunk's first token) plus 32-bit lane offsets.
+  auto stage_load = [&](int c) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(c) * kTC;
+    const char* xb = reinterpret_cast<const char*>(pipe::uniform_ptr(xg + t0 * C));
+    const char* db = reinterpret_cast<const char*>(pipe::uniform_ptr(dog + t0 * C));
+    const char* mb = reinterpret_cast<const char*>(pipe::uniform_ptr(a.mean + t0));
+    const char* rb = reinterpret_cast<const char*>(pipe::uniform_ptr(a.rstd + t0));
+    const int tmax = static_cast<int>(t_end - 1 - t0);
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
-      const int idx = tid + i * kThreads;
-      const int t = idx / XPL, j = idx - (idx / XPL) * XPL;
-      const int64_t tok = t0 + t;
-      if (tok < t_end) {
-        xr[i] = *reinterpret_cast<const u32x4*>(xg + tok * C + 8 * j);
-        dr[i] = *reinterpret_cast<const u32x4*>(dog + tok * C + 8 * j);
-        xm[i] = a.mean[tok];
-        xs[i] = a.rstd[tok];
-      } else {
-        xr[i] = dr[i] = u32x4{0, 0, 0, 0};
-        xm[i] = xs[i] = 0.f;
-      }
+      const int idx = ctid + i * CTHREADS;
+      const int t = min(idx / XPL, tmax), jj = idx - (idx / XPL) * XPL;
+      const uint32_t off = static_cast<uint32_t>(t * (2 * C) + 16 * jj);
+      xr[i] = *reinterpret_cast<const u32x4*>(xb + off);
+      dr[i] = *reinterpret_cast<const u32x4*>(db + off);
+      xm[i] = *reinterpret_cast<const float*>(mb + 4u * static_cast<uint32_t>(t));
+      xs[i] = *reinterpret_cast<const float*>(rb + 4u * static_cast<uint32_t>(t));
     }
   };
-  auto store = [&](int stage) {
-    char* sx = lds + W::S0 + stage * W::STAGE;
+  auto stage_store = [&](int c) {
+    char* sx = lds + (stage_x(c) - base);
     char* sd = sx + kTC * PX;
+    const int64_t t0 = t_begin + static_cast<int64_t>(c) * kTC;
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
-      const int idx = tid + i * kThreads;
-      const int t = idx / XPL, j = idx - (idx / XPL) * XPL;
+      const int idx = ctid + i * CTHREADS;
+      const int t = idx / XPL, jj = idx - (idx / XPL) * XPL;
+      const bool in = t0 + t < t_end;
       u32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        o[e] = pack_bf16((lo_bf16(xr[i][e]) - xm[i]) * xs[i], (hi_bf16(xr[i][e]) - xm[i]) * xs[i]);
-      *reinterpret_cast<u32x4*>(sx + t * PX + 16 * j) = o;
-      *reinterpret_cast<u32x4*>(sd + t * PX + 16 * j) = dr[i];
+        o[e] = in ? pack_bf16((lo_bf16(xr[i][e]) - xm[i]) * xs[i], (hi_bf16(xr[i][e]) - xm[i]) * xs[i]) : 0u;
+      *reinterpret_cast<u32x4*>(sx + t * PX + 16 * jj) = o;
+      *reinterpret_cast<u32x4*>(sd + t * PX + 16 * jj) = in ? dr[i] : u32x4{0, 0, 0, 0};
     }
   };
-  // Exchange slot of (job, quantity 0 da / 1 db / 2 h, k-step) for one lane.
-  auto xslot = [&](int job, int q, int kk) { return W::X0 + ((job * 3 + q) * 2 + kk) * 1024 + 16 * lane; };
 
-  f32x16 acc[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
-  float sacc = 0.f, sbcc = 0.f;  // phase-A waves: per-lane partial sums of da and db
-
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    const int stage = ch & 1;
-    if (ch + 1 < nch) load(ch + 1);
-    const uint32_t sx = base + W::S0 + stage * W::STAGE;
-    const uint32_t sd = sx + kTC * PX;
-    const char* sxp = lds + W::S0 + stage * W::STAGE;
-    const char* sdp = sxp + kTC * PX;
-
-    // Phase A: waves 0..3 each take (32 hidden units ht, 32 tokens sub) and form
-    // a, b, dh as D[token][hidden], then da, db, h as token-contracted operands.
-    if (wave < 4) {
-      const int ht = wave & 1, sub = wave >> 1;
-      const int trow = sub * 32 + li;
-      const char* wa_row = lds + W::W0 + L::WA + (32 * ht + li) * L::PW + 16 * half;
-      const char* wb_row = lds + W::W0 + L::WB + (32 * ht + li) * L::PW + 16 * half;
-      f32x16 fa = {}, fb = {}, fd = {};
+  // The two groups run separate loops (disjoint registers) that meet at the same
+  // barriers: two in the prologue, one per step, one before the range sums.
+  float* sums = reinterpret_cast<float*>(lds + W::SUMS);  // [job][a/b][32]
+  if (is_a) {
+    // Phase-A state: this lane's hidden unit j (B-operand column), its weights over
+    // the k slots 16 ks + 8 half + 0..7 (w_a, w_b scaled by gamma; w_out as is),
+    // and the constants w_a beta, w_b beta.
+    const int ht = wave & 1, sub = wave >> 1;
+    u32x4 wa_op[KS], wb_op[KS], wo_op[KS];
+    float ca = 0.f, cb = 0.f;
+    {
+      const int j = h0 + 32 * ht + li;
+      const uint16_t* wa_g = static_cast<const uint16_t*>(a.w_a) + static_cast<int64_t>(j) * C;
+      const uint16_t* wb_g = static_cast<const uint16_t*>(a.w_b) + static_cast<int64_t>(j) * C;
+      const uint16_t* wo_g = static_cast<const uint16_t*>(a.w_out);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        // y[token][16 ks + 8 half + 0..7] from the staged xhat row.
-        const u32x4 xh = *reinterpret_cast<const u32x4*>(sxp + trow * PX + 2 * (16 * ks + 8 * half));
         const int c0 = 16 * ks + 8 * half;
-        u32x4 y;
+        const u32x4 ra = *reinterpret_cast<const u32x4*>(wa_g + c0);
+        const u32x4 rb = *reinterpret_cast<const u32x4*>(wb_g + c0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          y[i] = pack_bf16(fmaf(lo_bf16(xh[i]), s_gamma[c0 + 2 * i], s_beta[c0 + 2 * i]),
-                           fmaf(hi_bf16(xh[i]), s_gamma[c0 + 2 * i + 1], s_beta[c0 + 2 * i + 1]));
-        fa = mma(y, *reinterpret_cast<const u32x4*>(wa_row + 32 * ks), fa);
-        fb = mma(y, *reinterpret_cast<const u32x4*>(wb_row + 32 * ks), fb);
-        // dout[token][16 ks + accumulator-row order] against w_out read transposed.
-        const char* drow = sdp + trow * PX + 2 * (16 * ks + 4 * half);
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(drow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(drow + 16);
-        fd = mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, tr(base + W::W0 + L::WO, L::PO, 16 * ks, 32 * ht), fd);
+        for (int i = 0; i < 4; ++i) {
+          const int c = c0 + 2 * i;
+          const float g0 = a.gamma[c], g1 = a.gamma[c + 1], b0 = a.beta[c], b1 = a.beta[c + 1];
+          const float a0 = lo_bf16(ra[i]), a1 = hi_bf16(ra[i]), e0 = lo_bf16(rb[i]), e1 = hi_bf16(rb[i]);
+          wa_op[ks][i] = pack_bf16(a0 * g0, a1 * g1);
+          wb_op[ks][i] = pack_bf16(e0 * g0, e1 * g1);
+          ca = fmaf(a0, b0, ca);
+          ca = fmaf(a1, b1, ca);
+          cb = fmaf(e0, b0, cb);
+          cb = fmaf(e1, b1, cb);
+          wo_op[ks][i] = static_cast<uint32_t>(wo_g[static_cast<int64_t>(c) * p.hidden + j]) |
+                         (static_cast<uint32_t>(wo_g[static_cast<int64_t>(c + 1) * p.hidden + j]) << 16);
+        }
       }
-      // Lane: hidden 32 ht + lane % 32; register v: token sub*32 + accumulator row v.
+      ca = pair_sum(ca);
+      cb = pair_sum(cb);
+    }
+    float sacc = 0.f, sbcc = 0.f;  // per-lane partial sums of da and db
+
+    // Phase A of chunk c: a, b, dh for (ht, sub), then da, db, h to the exchange.
+    auto phase_a = [&](int c) {
+      const uint32_t sx = stage_x(c), sd = sx + kTC * PX;
+      const uint32_t row = (sub * 32 + li) * PX + 16 * half;
+      f32x16 fa, fb, fd = {};
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        fa[v] = ca;
+        fb[v] = cb;
+      }
+      // Every operand read of the chunk is issued before the products, so that
+      // the reads' latency is paid once.
+      u32x4 xo[KS], dq[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        xo[ks] = pipe::lds_load16(sx + row + 32 * ks);
+        dq[ks] = pipe::lds_load16(sd + row + 32 * ks);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        fa = mma(xo[ks], wa_op[ks], fa);
+        fb = mma(xo[ks], wb_op[ks], fb);
+        fd = mma(dq[ks], wo_op[ks], fd);
+      }
+      // Lane: hidden 32 ht + lane % 32; register v: token sub * 32 + accumulator row
+      // v.  Tokens past the range hold xhat = dout = 0: dh = 0, so da = db = 0 there.
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 oa, ob, oh;
@@ -402,9 +440,9 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int v = 8 * kk + 2 * i + e;
-            const float s = sigmoid_f(fa[v]);
-            const float sl = fa[v] * s;
-            va[e] = fd[v] * fb[v] * (s * fmaf(fa[v], 1.f - s, 1.f));
+            const float sg = sigmoid_f(fa[v]);
+            const float sl = fa[v] * sg;
+            va[e] = fd[v] * fb[v] * (sg * fmaf(fa[v], 1.f - sg, 1.f));
             vb[e] = fd[v] * sl;
             vh[e] = sl * fb[v];
             sacc += va[e];
@@ -414,76 +452,118 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
           ob[i] = pack_bf16(vb[0], vb[1]);
           oh[i] = pack_bf16(vh[0], vh[1]);
         }
-        const int job = wave;
-        *reinterpret_cast<u32x4*>(lds + xslot(job, 0, kk)) = oa;
-        *reinterpret_cast<u32x4*>(lds + xslot(job, 1, kk)) = ob;
-        *reinterpret_cast<u32x4*>(lds + xslot(job, 2, kk)) = oh;
+        *reinterpret_cast<u32x4*>(lds + xslot(c, wave, 0, kk)) = oa;
+        *reinterpret_cast<u32x4*>(lds + xslot(c, wave, 1, kk)) = ob;
+        *reinterpret_cast<u32x4*>(lds + xslot(c, wave, 2, kk)) = oh;
       }
-    }
-    __syncthreads();
+    };
 
-    // Phase C: product tiles over the chunk's 64 tokens (four 16-token k-steps).
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tl = wave + kWaves * i;
-      if (tl < NT) {
-        const int q = tl / (2 * CT);
-        const int rem = tl - q * (2 * CT);
-        const int ht = rem / CT, ct = rem - (rem / CT) * CT;
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const int sub = k4 >> 1, kk = k4 & 1;
-          const int job = ht + 2 * sub;
-          if (q < 2) {
-            // M[hidden][c] += (da or db)[hidden][token] xhat[token][c]
-            const u32x4 av = *reinterpret_cast<const u32x4*>(lds + xslot(job, q, kk));
-            acc[i] = mma(av, tr(sx, PX, 32 * sub + 16 * kk, 32 * ct), acc[i]);
-          } else {
-            // Mo[c][hidden] += dout[token][c]^T h[token][hidden]
-            const u32x4 hv = *reinterpret_cast<const u32x4*>(lds + xslot(job, 2, kk));
-            acc[i] = mma(tr(sd, PX, 32 * sub + 16 * kk, 32 * ct), hv, acc[i]);
-          }
-        }
-      }
-    }
-    if (ch + 1 < nch) store(stage ^ 1);
+    __syncthreads();  // chunk 0 staged
+    phase_a(0);
     __syncthreads();
-  }
-
-  // Partial sums of this range: M_a, M_b [hidden][C], Mo [C][hidden], s_a, s_b [hidden].
-  const int h0 = group * kHC;
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int tl = wave + kWaves * i;
-    if (tl < NT) {
-      const int q = tl / (2 * CT);
-      const int rem = tl - q * (2 * CT);
-      const int ht = rem / CT, ct = rem - (rem / CT) * CT;
-      if (q < 2) {
-        float* dst = (q == 0 ? ma : mb) + (static_cast<int64_t>(range) * p.hidden + h0 + 32 * ht) * C + 32 * ct + li;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dst[static_cast<int64_t>(acc_row(v, lane)) * C] = acc[i][v];
-      } else {
-        float* dst = mo + (static_cast<int64_t>(range) * C + 32 * ct) * p.hidden + h0 + 32 * ht + li;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dst[static_cast<int64_t>(acc_row(v, lane)) * p.hidden] = acc[i][v];
-      }
+    for (int s = 0; s < nch; ++s) {
+      if (s + 1 < nch) phase_a(s + 1);
+      __syncthreads();
     }
-  }
-  float* sums = reinterpret_cast<float*>(lds + W::SUMS);  // [job][a/b][32]
-  if (wave < 4) {
     const float ta = pair_sum(sacc), tb = pair_sum(sbcc);
     if (half == 0) {
       sums[(wave * 2 + 0) * 32 + li] = ta;
       sums[(wave * 2 + 1) * 32 + li] = tb;
     }
+  } else {
+    // Phase C of chunk c over the chunk's 64 tokens (four 16-token k-steps).  Wave
+    // cw owns tiles cw + 4 i of the list (M_a tiles, M_b tiles, Mo tiles, 2 CT
+    // each): i < CT / 2 are M_a tiles, whose M_b partners i + CT / 2 cover the same
+    // (hidden, channel) block and share its xhat operands; i >= CT are Mo tiles.
+    // Each group's operand reads are issued before its products.
+    const int cw = wave - 4;
+    f32x16 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
+    auto phase_c = [&](int c) {
+      const uint32_t sx = stage_x(c), sd = sx + kTC * PX;
+#pragma unroll
+      for (int pr = 0; pr < CT / 2; ++pr) {
+        const int rem = cw + 4 * pr;
+        const int tht = rem / CT, ct = rem - (rem / CT) * CT;
+        u32x4 xop[4], av[4], bv[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int tsub = k4 >> 1, kk = k4 & 1, job = tht + 2 * tsub;
+          xop[k4] = tr(sx, PX, 32 * tsub + 16 * kk, 32 * ct);
+          av[k4] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 0, kk));
+          bv[k4] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 1, kk));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // M_a, M_b [hidden][c] += (da, db)[hidden][token] xhat[token][c]
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          acc[pr] = mma(av[k4], xop[k4], acc[pr]);
+          acc[pr + CT / 2] = mma(bv[k4], xop[k4], acc[pr + CT / 2]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int m = 0; m < CT / 2; ++m) {
+        const int rem = cw + 4 * m;
+        const int tht = rem / CT, ct = rem - (rem / CT) * CT;
+        u32x4 dop[4], hv[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int tsub = k4 >> 1, kk = k4 & 1, job = tht + 2 * tsub;
+          dop[k4] = tr(sd, PX, 32 * tsub + 16 * kk, 32 * ct);
+          hv[k4] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 2, kk));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Mo[c][hidden] += dout[token][c]^T h[token][hidden]
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) acc[CT + m] = mma(dop[k4], hv[k4], acc[CT + m]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // Chunk c is loaded during step c - 3 (after that step's store) and staged
+    // during step c - 2, so its loads have a barrier and a phase C to land.
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
+    if (nch > 1) {
+      stage_load(1);
+      stage_store(1);
+    }
+    if (nch > 2) stage_load(2);
+    __syncthreads();
+    for (int s = 0; s < nch; ++s) {
+      phase_c(s);
+      if (s + 2 < nch) stage_store(s + 2);
+      if (s + 3 < nch) stage_load(s + 3);
+      __syncthreads();
+    }
+    // Partial sums of this range: M_a, M_b [hidden][C], Mo [C][hidden].
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int q = (4 * i) / (2 * CT);
+      const int rem = cw + 4 * i - q * (2 * CT);
+      const int tht = rem / CT, ct = rem - (rem / CT) * CT;
+      if (q < 2) {
+        float* dst = (q == 0 ? ma : mb) + (static_cast<int64_t>(range) * p.hidden + h0 + 32 * tht) * C + 32 * ct + li;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[static_cast<int64_t>(acc_row(v, lane)) * C] = acc[i][v];
+      } else {
+        float* dst = mo + (static_cast<int64_t>(range) * C + 32 * ct) * p.hidden + h0 + 32 * tht + li;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[static_cast<int64_t>(acc_row(v, lane)) * p.hidden] = acc[i][v];
+      }
+    }
   }
   __syncthreads();
+  // Range sums s_a, s_b [hidden]: jobs tht (tokens 0..31 of each chunk) then tht + 2.
   if (tid < kHC) {
-    const int ht = tid >> 5, l = tid & 31;
-    // jobs ht (tokens 0..31 of each chunk) then ht + 2 (tokens 32..63)
-    sa[static_cast<int64_t>(range) * p.hidden + h0 + tid] = sums[(ht * 2 + 0) * 32 + l] + sums[((ht + 2) * 2 + 0) * 32 + l];
-    sb[static_cast<int64_t>(range) * p.hidden + h0 + tid] = sums[(ht * 2 + 1) * 32 + l] + sums[((ht + 2) * 2 + 1) * 32 + l];
+    const int tht = tid >> 5, l = tid & 31;
+    sa[static_cast<int64_t>(range) * p.hidden + h0 + tid] =
+        sums[(tht * 2 + 0) * 32 + l] + sums[((tht + 2) * 2 + 0) * 32 + l];
+    sb[static_cast<int64_t>(range) * p.hidden + h0 + tid] =
+        sums[(tht * 2 + 1) * 32 + l] + sums[((tht + 2) * 2 + 1) * 32 + l];
   }
 }
 

@@ -19,7 +19,8 @@
 //      tokens on the accumulator rows, so da, db and h leave the registers as
 //      operands whose contraction index is the token; they are exchanged through
 //      LDS and accumulated into M_a, M_b and dout^T h against xhat and dout staged
-//      per 64 tokens.  The hidden groups of one range share an XCD.
+//      per 64 tokens, by a second group of waves one chunk behind the first.  The
+//      hidden groups of one range share an XCD.
 //   3. Finalize: partials summed in fixed slots of ranges (each in increasing order), dw_a,
 //      dw_b, dw_out, and dgamma / dbeta by fixed-shape sums.
 // Nothing of size tokens x hidden is written to memory; every sum has a fixed order.

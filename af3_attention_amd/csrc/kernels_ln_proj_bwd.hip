@@ -73,6 +73,7 @@ __host__ __device__ __forceinline__ int bias_width(const ProjProblem& p) {
 struct GSource {
   const uint16_t* base;  // element (tok, o0) at base + tok * pitch
   int pitch;
+  bool ok;               // false past the outputs: base is x (always present), values are 0
 };
 __device__ __forceinline__ GSource g_source(const ProjProblem& p, const ProjBwdArgs& a, const uint16_t* gb,
                                             int o0) {
@@ -80,14 +81,15 @@ __device__ __forceinline__ GSource g_source(const ProjProblem& p, const ProjBwdA
   if (o0 < p.n_qkv) {
     const int which = o0 / hd;
     const uint16_t* src = static_cast<const uint16_t*>(which == 0 ? a.dq : (which == 1 ? a.dk : a.dv));
-    return GSource{src + (o0 - which * hd), hd};
+    return GSource{src + (o0 - which * hd), hd, true};
   }
   const int hb = bias_width(p);
-  if (o0 < p.n_qkv + hb) return GSource{gb + (o0 - p.n_qkv), hb};
-  return GSource{nullptr, 0};
+  if (o0 < p.n_qkv + hb) return GSource{gb + (o0 - p.n_qkv), hb, true};
+  return GSource{static_cast<const uint16_t*>(a.x), 0, false};  // x is always present
 }
+// Loaded unconditionally (no branch around the load); the caller applies ok.
 __device__ __forceinline__ u32x4 g_load(const GSource& g, int64_t tok) {
-  return g.base ? *reinterpret_cast<const u32x4*>(g.base + tok * g.pitch) : u32x4{0, 0, 0, 0};
+  return *reinterpret_cast<const u32x4*>(g.base + tok * g.pitch);
 }
 
 // The pair-bias gradient (fp32, [H][A][B] in the attention's frame) in token
@@ -330,31 +332,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
     u32x4 x[NXP];
     float m[NXP], r[NXP];
   };
+  // Tokens past the range are loaded from its last token (no branch around the
+  // loads) and staged as zeros.  The store also adds the staged G values to this
+  // thread's column sums (its 8 outputs, summed over its tokens in order).
   auto load = [&](int ch, Regs& R) {
     const int64_t t0 = t_begin + static_cast<int64_t>(ch) * kChunk;
 #pragma unroll
     for (int i = 0; i < NGP; ++i) {
-      const int64_t tok = t0 + (tid + i * kThreads) / GPL;
-      R.g[i] = tok < t_end ? g_load(gsrc, tok) : u32x4{0, 0, 0, 0};
+      const int64_t tok = min(t0 + (tid + i * kThreads) / GPL, t_end - 1);
+      R.g[i] = g_load(gsrc, tok);
     }
 #pragma unroll
     for (int i = 0; i < NXP; ++i) {
       const int idx = tid + i * kThreads;
       const int t = idx / XPL;
       const int j = idx - t * XPL;
-      const int64_t tok = t0 + t;
-      if (idx < XP && tok < t_end) {
+      const int64_t tok = min(t0 + t, t_end - 1);
+      if (XP % kThreads == 0 || idx < XP) {
         R.x[i] = *reinterpret_cast<const u32x4*>(xg + tok * C + 8 * j);
         R.m[i] = a.mean[tok];
         R.r[i] = a.rstd[tok];
-      } else {
-        R.x[i] = u32x4{0, 0, 0, 0};
-        R.m[i] = 0.f;
-        R.r[i] = 0.f;
       }
     }
   };
-  auto store = [&](const Regs& R, int buf) {
+  float s_part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto store = [&](const Regs& R, int ch, int buf) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(ch) * kChunk;
     char* sg = lds + buf * STAGE;
     char* sx = sg + kChunk * PG;
 #pragma unroll
@@ -362,18 +365,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
       const int idx = tid + i * kThreads;
       const int t = idx / GPL;
       const int j = idx - t * GPL;
-      *reinterpret_cast<u32x4*>(sg + t * PG + 16 * j) = R.g[i];
+      const u32x4 gv = (gsrc.ok && t0 + t < t_end) ? R.g[i] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(sg + t * PG + 16 * j) = gv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s_part[2 * e] += lo_bf16(gv[e]);
+        s_part[2 * e + 1] += hi_bf16(gv[e]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NXP; ++i) {
       const int idx = tid + i * kThreads;
-      if (idx < XP) {
+      if (XP % kThreads == 0 || idx < XP) {
         const int t = idx / XPL;
         const int j = idx - t * XPL;
+        const bool in = t0 + t < t_end;
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          o[e] = pack_bf16((lo_bf16(R.x[i][e]) - R.m[i]) * R.r[i], (hi_bf16(R.x[i][e]) - R.m[i]) * R.r[i]);
+          o[e] = in ? pack_bf16((lo_bf16(R.x[i][e]) - R.m[i]) * R.r[i], (hi_bf16(R.x[i][e]) - R.m[i]) * R.r[i]) : 0u;
         *reinterpret_cast<u32x4*>(sx + t * PX + 16 * j) = o;
       }
     }
@@ -390,26 +400,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
+  // The wave's two product tiles wave and wave + kWaves; a tile past the group's
+  // last (in a group of fewer than four output tiles) repeats the last one and is
+  // not stored, so the loop has no branches.
   f32x16 acc[2] = {f32x16{}, f32x16{}};
-  float s_acc = 0.f;
+  int t_ot[2], t_ct[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tl = min(wave + kWaves * tt, ntile - 1);
+    t_ot[tt] = tl / CT;
+    t_ct[tt] = tl - t_ot[tt] * CT;
+  }
   auto compute = [&](int buf) {
     const uint32_t sg = lds0 + buf * STAGE;
     const uint32_t sx = sg + kChunk * PG;
-    if (tid < 32 * n_ot_g) {
-      const uint16_t* col = reinterpret_cast<const uint16_t*>(lds + buf * STAGE) + tid;
-#pragma unroll 8
-      for (int t = 0; t < kChunk; ++t) s_acc += bf16_to_f32(col[t * (PG / 2)]);
-    }
 #pragma unroll 2
     for (int kk = 0; kk < kChunk / 16; ++kk)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int tl = wave + kWaves * tt;
-        if (tl < ntile) {
-          const int ot = tl / CT, ct = tl - (tl / CT) * CT;
-          acc[tt] = mma(tr(sg, PG, 32 * ot, kk), tr(sx, PX, 32 * ct, kk), acc[tt]);
-        }
-      }
+      for (int tt = 0; tt < 2; ++tt)
+        acc[tt] = mma(tr(sg, PG, 32 * t_ot[tt], kk), tr(sx, PX, 32 * t_ct[tt], kk), acc[tt]);
   };
 
   // Chunk ch is staged in LDS buffer ch % 2; register set A carries even chunks,
@@ -417,17 +426,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
   Regs RA, RB;
   load(0, RA);
   if (nch > 1) load(1, RB);
-  store(RA, 0);
+  store(RA, 0, 0);
   __syncthreads();
   for (int ch = 0; ch < nch; ch += 2) {
     compute(0);
     if (ch + 2 < nch) load(ch + 2, RA);
-    if (ch + 1 < nch) store(RB, 1);
+    if (ch + 1 < nch) store(RB, ch + 1, 1);
     __syncthreads();
     if (ch + 1 >= nch) break;
     compute(1);
     if (ch + 3 < nch) load(ch + 3, RB);
-    if (ch + 2 < nch) store(RA, 0);
+    if (ch + 2 < nch) store(RA, ch + 2, 0);
     __syncthreads();
   }
 
@@ -443,7 +452,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_mpart_mfma(ProjProblem p, Pro
       for (int v = 0; v < 16; ++v) dst[static_cast<int64_t>(acc_row(v, lane)) * C] = acc[tt][v];
     }
   }
-  if (tid < 32 * n_ot_g) spart[static_cast<int64_t>(range) * po + 32 * ot0 + tid] = s_acc;
+  // Column sums: thread tid holds outputs 8 (tid % GPL) + 0..7 of the group; the
+  // kThreads / GPL threads of each output set are added in increasing order.
+  constexpr int NSET = kThreads / GPL;
+  float* sred = reinterpret_cast<float*>(lds);  // [NSET][kGroupOut], the stages are free
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sred[(tid / GPL) * kGroupOut + 8 * (tid % GPL) + e] = s_part[e];
+  __syncthreads();
+  if (tid < 32 * n_ot_g) {
+    float sum = 0.f;
+    for (int m = 0; m < NSET; ++m) sum += sred[m * kGroupOut + tid];
+    spart[static_cast<int64_t>(range) * po + 32 * ot0 + tid] = sum;
+  }
 }
 
 // ---------------------------------------------------------------- vector kernels

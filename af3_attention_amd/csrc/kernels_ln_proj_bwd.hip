@@ -202,8 +202,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBw
         }
       }
     };
-    // Every k-step's upstream gradients are one 16-byte load; a batch (up to NB
-    // k-steps, normally the whole tile) is issued before its first product.
+    // Every k-step's upstream gradients are one 16-byte load; the batch (the whole
+    // tile) and the tile's x and statistics are issued before the first product.
+    // Loads are unconditional: a padding lane reads token 0 and its results are
+    // never stored.
+    u32x2 xr[CT][4];
+    float mean, rstd;
     {
       constexpr int NQ = 3 * HDK;
       static_assert(HDK > 0 && NQ + 1 <= NB, "q/k/v and bias k-steps must fit the register batch");
@@ -213,24 +217,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBw
 #pragma unroll
       for (int w3 = 0; w3 < 3; ++w3)
 #pragma unroll
-        for (int c = 0; c < HDK; ++c)
-          gq[w3 * HDK + c] = valid ? *reinterpret_cast<const u32x4*>(rows[w3] + 16 * c) : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < HDK; ++c) gq[w3 * HDK + c] = *reinterpret_cast<const u32x4*>(rows[w3] + 16 * c);
       const bool has_bias = hb > 0;
-      gq[NQ] = (valid && has_bias) ? *reinterpret_cast<const u32x4*>(gb + tk * hb + 8 * half) : u32x4{0, 0, 0, 0};
+      gq[NQ] = has_bias ? *reinterpret_cast<const u32x4*>(gb + tk * hb + 8 * half) : u32x4{0, 0, 0, 0};
+      // x at the accumulator's channels (32 ct + 8 g + 4 half + 0..3).
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          xr[ct][g] = *reinterpret_cast<const u32x2*>(xg + tk * C + 32 * ct + 8 * g + 4 * half);
+      mean = a.mean[tk];
+      rstd = a.rstd[tk];
       run_steps(has_bias ? NQ + 1 : NQ, gq);
     }
-
-    // x at the accumulator's channels (32 ct + 8 g + 4 half + 0..3), requested after
-    // the products so that the upstream gradients alone occupy the load registers.
-    u32x2 xr[CT][4];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        xr[ct][g] = valid ? *reinterpret_cast<const u32x2*>(xg + tk * C + 32 * ct + 8 * g + 4 * half)
-                          : u32x2{0, 0};
-    const float mean = valid ? a.mean[tk] : 0.f;
-    const float rstd = valid ? a.rstd[tk] : 0.f;
 
     // Layer-norm backward on the token's channels (this lane's half, then the partner's).
     float s1 = 0.f, s2 = 0.f;

@@ -174,8 +174,12 @@ def check_bwd(inp, ia=None, ib=None):
 
 
 @pytest.mark.parametrize("A,B,C,n", [(16, 16, 128, 4), (7, 9, 128, 4), (33, 20, 64, 4), (5, 5, 128, 1),
-                                     (12, 11, 64, 2), (1, 1, 128, 4), (40, 41, 128, 4), (70, 70, 64, 4)])
+                                     (12, 11, 64, 2), (1, 1, 128, 4), (40, 41, 128, 4), (70, 70, 64, 4),
+                                     (72, 72, 128, 4), (100, 100, 128, 4), (50, 90, 64, 4)])
 def test_bwd_shapes(A, B, C, n):
+    """Ragged tiles and token ranges; the weight-gradient kernel's per-range chunk
+    counts cover 1, 2, 3 and 5 (with a shorter last range and a partial last chunk),
+    besides the full-size cases below."""
     banner(f"bwd A={A} B={B} C={C} n={n}")
     check_bwd(generate_transition(A, B, C, n, dtype=torch.bfloat16, seed=A * 7 + n))
 

@@ -170,30 +170,76 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBw
   const uint16_t* const dkg = static_cast<const uint16_t*>(a.dk);
   const uint16_t* const dvg = static_cast<const uint16_t*>(a.dv);
 
-  for (int tile = blockIdx.x * kWaves + wave; tile < p.tiles; tile += stride) {
+  // A tile's k-steps (q, k, v by 16-output steps, then the bias step) in two
+  // register batches: batch 1 of a tile is requested, with its x and statistics, as
+  // the tile starts; batch 0 of the next tile as soon as this tile's batch 0 has
+  // been used.  So every batch's loads overlap half a tile's products (and the norm
+  // backward), and the two batches together hold what one whole tile did.  Loads
+  // are unconditional: a padding lane reads token 0 and its results are never stored.
+  constexpr int NQ = 3 * HDK;
+  constexpr int NK = NQ + 1;
+  constexpr int N0 = (NK + 1) / 2, N1 = NK - N0;  // batch 1 ends with the bias step
+  static_assert(HDK > 0 && NK <= NB, "q/k/v and bias k-steps must fit the register batches");
+  const bool has_bias = hb > 0;
+  auto token_of = [&](int tl) {
+    const int64_t t = tile_token(p, tl, li);
+    return t >= 0 ? t : int64_t{0};
+  };
+  auto load_step = [&](int j, int64_t tk, u32x4& g) {  // j is a compile-time constant after unrolling
+    if (j < NQ) {
+      const int w3 = j / HDK, c = j - (j / HDK) * HDK;
+      const uint16_t* src = w3 == 0 ? dqg : (w3 == 1 ? dkg : dvg);
+      g = *reinterpret_cast<const u32x4*>(src + tk * (16 * HDK) + 8 * half + 16 * c);
+    } else {
+      g = has_bias ? *reinterpret_cast<const u32x4*>(gb + tk * hb + 8 * half) : u32x4{0, 0, 0, 0};
+    }
+  };
+  u32x4 g0[N0], g1[N1];
+  auto load_batch0 = [&](int64_t tk) {
+#pragma unroll
+    for (int j = 0; j < N0; ++j) load_step(j, tk, g0[j]);
+  };
+  auto load_batch1 = [&](int64_t tk) {
+#pragma unroll
+    for (int j = 0; j < N1; ++j) load_step(N0 + j, tk, g1[j]);
+  };
+  // W^T operands of k-step ks for every channel tile.
+  auto read_w = [&](int ks, u32x4* w) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      w[ct] = *reinterpret_cast<const u32x4*>(s_wt + (32 * ct + li) * pw + (16 * ks + 8 * half) * 2);
+  };
+
+  int tile = blockIdx.x * kWaves + wave;
+  if (tile < p.tiles) load_batch0(token_of(tile));
+  for (; tile < p.tiles; tile += stride) {
     const int64_t tok = tile_token(p, tile, li);
     const bool valid = tok >= 0;
     const int64_t tk = valid ? tok : 0;
+    load_batch1(tk);
+    // x at the accumulator's channels (32 ct + 8 g + 4 half + 0..3).
+    u32x2 xr[CT][4];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) xr[ct][g] = *reinterpret_cast<const u32x2*>(xg + tk * C + 32 * ct + 8 * g + 4 * half);
+    const float mean = a.mean[tk];
+    const float rstd = a.rstd[tk];
 
     // dy^T tile per 32 channels: D[c][t] = sum_o W^T[c][o] G[t][o].
     f32x16 acc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x16{};
-    // W^T operands of k-step ks for every channel tile.
-    auto read_w = [&](int ks, u32x4* w) {
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        w[ct] = *reinterpret_cast<const u32x4*>(s_wt + (32 * ct + li) * pw + (16 * ks + 8 * half) * 2);
-    };
-    // Products of k-steps 0 .. n-1: each step's W^T reads are issued one step ahead,
-    // and a scheduling barrier keeps the compiler from hoisting more of them.
-    auto run_steps = [&](int n, const u32x4* g) {
+    // Products of k-steps K0 .. K0 + n - 1: each step's W^T reads are issued one
+    // step ahead, and a scheduling barrier keeps the compiler from hoisting more.
+    auto run_steps = [&](auto k0_c, auto nmax_c, int n, const u32x4* g) {
+      constexpr int K0 = decltype(k0_c)::value, NMAX = decltype(nmax_c)::value;
       u32x4 wc[CT], wn[CT];
-      read_w(0, wc);
+      read_w(K0, wc);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
+      for (int j = 0; j < NMAX; ++j) {
         if (j < n) {
-          if (j + 1 < n) read_w(j + 1, wn);
+          if (j + 1 < n) read_w(K0 + j + 1, wn);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) acc[ct] = mma(wc[ct], g[j], acc[ct]);
           __builtin_amdgcn_sched_barrier(0);
@@ -202,34 +248,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBw
         }
       }
     };
-    // Every k-step's upstream gradients are one 16-byte load; the batch (the whole
-    // tile) and the tile's x and statistics are issued before the first product.
-    // Loads are unconditional: a padding lane reads token 0 and its results are
-    // never stored.
-    u32x2 xr[CT][4];
-    float mean, rstd;
-    {
-      constexpr int NQ = 3 * HDK;
-      static_assert(HDK > 0 && NQ + 1 <= NB, "q/k/v and bias k-steps must fit the register batch");
-      u32x4 gq[NB];
-      const int64_t oq = tk * (16 * HDK) + 8 * half;
-      const uint16_t* rows[3] = {dqg + oq, dkg + oq, dvg + oq};
-#pragma unroll
-      for (int w3 = 0; w3 < 3; ++w3)
-#pragma unroll
-        for (int c = 0; c < HDK; ++c) gq[w3 * HDK + c] = *reinterpret_cast<const u32x4*>(rows[w3] + 16 * c);
-      const bool has_bias = hb > 0;
-      gq[NQ] = has_bias ? *reinterpret_cast<const u32x4*>(gb + tk * hb + 8 * half) : u32x4{0, 0, 0, 0};
-      // x at the accumulator's channels (32 ct + 8 g + 4 half + 0..3).
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          xr[ct][g] = *reinterpret_cast<const u32x2*>(xg + tk * C + 32 * ct + 8 * g + 4 * half);
-      mean = a.mean[tk];
-      rstd = a.rstd[tk];
-      run_steps(has_bias ? NQ + 1 : NQ, gq);
-    }
+    run_steps(std::integral_constant<int, 0>(), std::integral_constant<int, N0>(), N0, g0);
+    if (tile + stride < p.tiles) load_batch0(token_of(tile + stride));
+    run_steps(std::integral_constant<int, N0>(), std::integral_constant<int, N1>(), has_bias ? N1 : N1 - 1, g1);
 
     // Layer-norm backward on the token's channels (this lane's half, then the partner's).
     float s1 = 0.f, s2 = 0.f;

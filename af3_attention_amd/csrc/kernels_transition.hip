@@ -9,11 +9,11 @@
 // HBM sees x in and out (and the per-token statistics) out; y, a, b and h live
 // in registers.
 //
-// bf16, C in {64, 128}.  A workgroup of 8 waves takes 256 tokens (one 32-token
-// tile per wave) at a time and streams the weights through LDS in chunks of 64
-// hidden units (w_a and w_b rows, the matching w_out columns), double-buffered:
-// every chunk is read once from L2 per 256 tokens, copied straight from global
-// memory into LDS.  Per chunk and 32 hidden
+// bf16, C in {64, 128}.  A workgroup of 12 (C = 128) or 8 (C = 64) waves takes
+// 384 or 256 tokens (one 32-token tile per wave) at a time and streams the
+// weights through LDS in chunks of 64 hidden units (w_a and w_b rows, the
+// matching w_out columns), double-buffered: every chunk is read once from L2 per
+// pass, copied straight from global memory into LDS.  Per chunk and 32 hidden
 // units a wave forms a and b on the matrix cores (D[hidden][token]), applies
 // the gate in registers, and the packed accumulator registers are directly the
 // B operand of out += w_out[:, chunk] h (the A operand reads w_out with the same
@@ -35,8 +35,16 @@ using namespace trans;
 using proj::hi_bf16;
 using proj::lo_bf16;
 
+// Waves per workgroup: 12 (three per SIMD) at C = 128, where the registers allow
+// it and the third wave per SIMD hides latency that two do not; 8 at C = 64, where
+// it measured slightly faster.
 template <int KS>
-__global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem p, TransFwdArgs a) {
+constexpr int fwd_waves() { return KS == 8 ? 12 : 8; }
+
+template <int KS>
+__global__ __launch_bounds__(64 * fwd_waves<KS>(), 1) void transition_fwd_mfma(TransProblem p, TransFwdArgs a) {
+  constexpr int kFwdWaves = fwd_waves<KS>();
+  constexpr int kFwdThreads = 64 * kFwdWaves;
   using L = TransLayout<KS>;
   constexpr int C = L::C;
   constexpr int CT = C / 32;
@@ -51,14 +59,14 @@ __global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem 
   const int half = lane >> 5;
   const int li = lane & 31;
   const int nch = p.hidden / kHC;
-  const int npass = (p.tiles + kWaves - 1) / kWaves;
+  const int npass = (p.tiles + kFwdWaves - 1) / kFwdWaves;
 
   const int wave_u = pipe::wave_id();
   const uint32_t wbuf_a = pipe::lds_addr(wbuf);
-  WeightCopy<KS> wc;
+  WeightCopy<KS, kFwdWaves> wc;
   wc.init(a.w_a, a.w_b, a.w_out, p.hidden, wave_u, lane);
 
-  for (int c = tid; c < C; c += kThreads) {
+  for (int c = tid; c < C; c += kFwdThreads) {
     s_gamma[c] = a.gamma[c];
     s_beta[c] = a.beta[c];
   }
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem 
   int buf = 0;
 
   for (int pass = first; pass < npass; pass += gridDim.x) {
-    const int64_t t = static_cast<int64_t>(pass * kWaves + wave) * 32 + li;
+    const int64_t t = static_cast<int64_t>(pass * kFwdWaves + wave) * 32 + li;
     const bool valid = t < p.T;
     const int64_t tok = valid ? t : 0;
 
@@ -186,6 +194,8 @@ __global__ __launch_bounds__(kThreads, 1) void transition_fwd_mfma(TransProblem 
 template <int KS>
 hipError_t launch_fwd(const TransProblem& p, const TransFwdArgs& a, hipStream_t s) {
   using L = TransLayout<KS>;
+  constexpr int kFwdWaves = fwd_waves<KS>();
+  constexpr int kFwdThreads = 64 * kFwdWaves;
   auto kern = transition_fwd_mfma<KS>;
   const size_t lds = L::lds_bytes();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -194,12 +204,12 @@ hipError_t launch_fwd(const TransProblem& p, const TransFwdArgs& a, hipStream_t 
   int dev = 0, cus = 0, per_cu = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds)) != hipSuccess) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFwdThreads, lds)) != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
-  const int npass = (p.tiles + kWaves - 1) / kWaves;
+  const int npass = (p.tiles + kFwdWaves - 1) / kFwdWaves;
   const int grid = npass < cus * per_cu ? npass : cus * per_cu;
   KernelTimer timer("transition_fwd", s);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, p, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFwdThreads), lds, s, p, a);
   return hipGetLastError();
 }
 

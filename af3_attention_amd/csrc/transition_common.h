@@ -40,13 +40,14 @@ __device__ __forceinline__ float silu(float a) {
 // matrix: a uniform base (the part's chunk) plus a per-lane byte offset that is
 // the same for every chunk.  A lane whose 16 bytes fall in a row's padding copies
 // the row's first 16 bytes (padding is never read).  The copies count in vmcnt:
-// a wave waits for its own copies, then a barrier publishes them.
-template <int KS>
+// a wave waits for its own copies, then a barrier publishes them.  NW waves share
+// the slices.
+template <int KS, int NW = kWaves>
 struct WeightCopy {
   using L = TransLayout<KS>;
   static constexpr int C = L::C;
   static constexpr int SLICES = L::CHUNK / 1024;
-  static constexpr int NIT = (SLICES + kWaves - 1) / kWaves;
+  static constexpr int NIT = (SLICES + NW - 1) / NW;
   static_assert(L::CHUNK % 1024 == 0 && L::WB % 1024 == 0 && L::WO % 1024 == 0,
                 "every part of the chunk image must be whole 1 KB slices");
   const char* wa;
@@ -65,7 +66,7 @@ struct WeightCopy {
     wo = static_cast<const char*>(w_out);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int slice = it * kWaves + wave;
+      const int slice = it * NW + wave;
       int o = slice * 1024 + 16 * lane;
       uint32_t v = 0;
       if (slice < SLICES) {
@@ -86,7 +87,7 @@ struct WeightCopy {
   __device__ __forceinline__ void issue(int ch, uint32_t dst, int wave) const {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int slice = it * kWaves + wave;
+      const int slice = it * NW + wave;
       if (slice >= SLICES) break;
       const int part = part_of(slice);
       const char* base = part == 0   ? wa + static_cast<int64_t>(ch) * (kHC * 2 * C)

@@ -161,10 +161,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_mfma(ProjProblem p, ProjBw
 
   const uint16_t* xg = static_cast<const uint16_t*>(a.x);
   uint16_t* dxg = static_cast<uint16_t*>(a.dx);
-  const int nks = ko / 16;  // <= NB (checked by the launcher)
   constexpr float inv_c = 1.0f / C;
   const int stride = gridDim.x * kWaves;
-  const int hd = p.H * p.D;
   const int hb = bias_width(p);
   const uint16_t* const dqg = static_cast<const uint16_t*>(a.dq);
   const uint16_t* const dkg = static_cast<const uint16_t*>(a.dk);
@@ -646,7 +644,7 @@ __global__ __launch_bounds__(kVecThreads) void bwd_finalize_cols(ProjProblem p, 
   sb[threadIdx.x] = b;
   __syncthreads();
   for (int w = kVecThreads / 2; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) {
+    if (static_cast<int>(threadIdx.x) < w) {
       sg[threadIdx.x] += sg[threadIdx.x + w];
       sb[threadIdx.x] += sb[threadIdx.x + w];
     }

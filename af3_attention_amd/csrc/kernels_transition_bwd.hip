@@ -677,7 +677,7 @@ __global__ __launch_bounds__(kFinThreads) void transition_fin_cols(TransProblem 
   sbb[threadIdx.x] = b;
   __syncthreads();
   for (int w = kFinThreads / 2; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) {
+    if (static_cast<int>(threadIdx.x) < w) {
       sg[threadIdx.x] += sg[threadIdx.x + w];
       sbb[threadIdx.x] += sbb[threadIdx.x + w];
     }

@@ -474,52 +474,49 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
   } else {
     // Phase C of chunk c over the chunk's 64 tokens (four 16-token k-steps).  Wave
     // cw owns tiles cw + 4 i of the list (M_a tiles, M_b tiles, Mo tiles, 2 CT
-    // each): i < CT / 2 are M_a tiles, whose M_b partners i + CT / 2 cover the same
-    // (hidden, channel) block and share its xhat operands; i >= CT are Mo tiles.
-    // Each group's operand reads are issued before its products.
+    // each): i < CT / 2 are M_a tiles, their M_b partners are i + CT / 2, and the Mo
+    // tiles of the same hidden half are i + CT.  Each group's operand reads are
+    // issued before its products.
     const int cw = wave - 4;
     f32x16 acc[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
+    // Every tile of this wave has the channel block ct = cw % CT ((cw + 4 i) % CT,
+    // with CT in {2, 4}), so each k-step's xhat and dout operands are read once and
+    // serve all of the wave's tiles of that k-step.
     auto phase_c = [&](int c) {
       const uint32_t sx = stage_x(c), sd = sx + kTC * PX;
+      const int ct = cw % CT;
 #pragma unroll
-      for (int pr = 0; pr < CT / 2; ++pr) {
-        const int rem = cw + 4 * pr;
-        const int tht = rem / CT, ct = rem - (rem / CT) * CT;
-        u32x4 xop[4], av[4], bv[4];
+      for (int hk = 0; hk < 2; ++hk) {  // token halves: k-steps 2 hk, 2 hk + 1
+        u32x4 xop[2], dop[2];
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const int tsub = k4 >> 1, kk = k4 & 1, job = tht + 2 * tsub;
-          xop[k4] = tr(sx, PX, 32 * tsub + 16 * kk, 32 * ct);
-          av[k4] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 0, kk));
-          bv[k4] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 1, kk));
+        for (int kk = 0; kk < 2; ++kk) {
+          xop[kk] = tr(sx, PX, 32 * hk + 16 * kk, 32 * ct);
+          dop[kk] = tr(sd, PX, 32 * hk + 16 * kk, 32 * ct);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // M_a, M_b [hidden][c] += (da, db)[hidden][token] xhat[token][c]
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          acc[pr] = mma(av[k4], xop[k4], acc[pr]);
-          acc[pr + CT / 2] = mma(bv[k4], xop[k4], acc[pr + CT / 2]);
+        for (int pr = 0; pr < CT / 2; ++pr) {
+          const int tht = (cw + 4 * pr) / CT;
+          const int job = tht + 2 * hk;
+          u32x4 av[2], bv[2], hv[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            av[kk] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 0, kk));
+            bv[kk] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 1, kk));
+            hv[kk] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 2, kk));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            // M_a, M_b [hidden][c] += (da, db)[hidden][token] xhat[token][c]
+            acc[pr] = mma(av[kk], xop[kk], acc[pr]);
+            acc[pr + CT / 2] = mma(bv[kk], xop[kk], acc[pr + CT / 2]);
+            // Mo[c][hidden] += dout[token][c]^T h[token][hidden]
+            acc[CT + pr] = mma(dop[kk], hv[kk], acc[CT + pr]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int m = 0; m < CT / 2; ++m) {
-        const int rem = cw + 4 * m;
-        const int tht = rem / CT, ct = rem - (rem / CT) * CT;
-        u32x4 dop[4], hv[4];
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const int tsub = k4 >> 1, kk = k4 & 1, job = tht + 2 * tsub;
-          dop[k4] = tr(sd, PX, 32 * tsub + 16 * kk, 32 * ct);
-          hv[k4] = *reinterpret_cast<const u32x4*>(lds + xslot(c, job, 2, kk));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // Mo[c][hidden] += dout[token][c]^T h[token][hidden]
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) acc[CT + m] = mma(dop[k4], hv[k4], acc[CT + m]);
-        __builtin_amdgcn_sched_barrier(0);
       }
     };
 

@@ -179,9 +179,10 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_dx(TransProblem p,
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int v = 8 * kk + 2 * i + e;
+              // silu(a) = a s, silu'(a) = s (1 + a (1 - s)) = s + silu(a) (1 - s)
               const float s = sigmoid_f(fa[v]);
               const float sl = fa[v] * s;
-              va[e] = fd[v] * fb[v] * (s * fmaf(fa[v], 1.f - s, 1.f));
+              va[e] = fd[v] * fb[v] * fmaf(-sl, s, s + sl);
               vb[e] = fd[v] * sl;
             }
             dab[kk][i] = pack_bf16(va[0], va[1]);
@@ -356,10 +357,11 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
       const int idx = ctid + i * CTHREADS;
       const int t = idx / XPL, jj = idx - (idx / XPL) * XPL;
       const bool in = t0 + t < t_end;
+      const float nm = -xm[i] * xs[i];  // xhat = x rstd - mean rstd
       u32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        o[e] = in ? pack_bf16((lo_bf16(xr[i][e]) - xm[i]) * xs[i], (hi_bf16(xr[i][e]) - xm[i]) * xs[i]) : 0u;
+        o[e] = in ? pack_bf16(fmaf(lo_bf16(xr[i][e]), xs[i], nm), fmaf(hi_bf16(xr[i][e]), xs[i], nm)) : 0u;
       *reinterpret_cast<u32x4*>(sx + t * PX + 16 * jj) = o;
       *reinterpret_cast<u32x4*>(sd + t * PX + 16 * jj) = in ? dr[i] : u32x4{0, 0, 0, 0};
     }
@@ -441,9 +443,10 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int v = 8 * kk + 2 * i + e;
+            // silu(a) = a s, silu'(a) = s + silu(a) (1 - s)
             const float sg = sigmoid_f(fa[v]);
             const float sl = fa[v] * sg;
-            va[e] = fd[v] * fb[v] * (sg * fmaf(fa[v], 1.f - sg, 1.f));
+            va[e] = fd[v] * fb[v] * fmaf(-sl, sg, sg + sl);
             vb[e] = fd[v] * sl;
             vh[e] = sl * fb[v];
             sacc += va[e];

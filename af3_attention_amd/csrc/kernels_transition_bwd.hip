@@ -72,7 +72,7 @@ struct TrRead {
 // ---------------------------------------------------------------- 1. dx
 
 template <int KS>
-__global__ __launch_bounds__(kThreads, 1) void transition_bwd_dx(TransProblem p, TransBwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void transition_bwd_dx(TransProblem p, TransBwdArgs a, uint16_t* xh_out) {
   using L = TransLayout<KS>;
   constexpr int C = L::C;
   constexpr int CT = C / 32;
@@ -116,20 +116,32 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_dx(TransProblem p,
     const float mean = valid ? a.mean[tok] : 0.f;
     const float rstd = valid ? a.rstd[tok] : 0.f;
 
-    // y as the B operand (k = channel, 8 consecutive per lane half).
+    // y as the B operand (k = channel, 8 consecutive per lane half), formed from
+    // xhat rounded to bf16: that rounded xhat goes to the workspace, where the
+    // weight-gradient pass stages it as it is and recomputes a and b from it, so
+    // both passes start from the same xhat.  The workspace holds whole passes:
+    // tokens past the end store their zeros there with no branch.  All x loads
+    // precede the stores (which may alias them as far as the compiler knows), and
+    // the stores drain under the first chunk's products.
     u32x4 yb[KS];
     {
       const u32x4* src = reinterpret_cast<const u32x4*>(xg + tok * C + 8 * half);
+      u32x4* xh_dst = reinterpret_cast<u32x4*>(xh_out + t * C + 8 * half);
+      u32x4 xr[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) xr[ks] = src[2 * ks];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 xr = valid ? src[2 * ks] : u32x4{0, 0, 0, 0};
         const int c0 = 16 * ks + 8 * half;
+        u32x4 xh;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float y0 = fmaf((lo_bf16(xr[i]) - mean) * rstd, s_gamma[c0 + 2 * i], s_beta[c0 + 2 * i]);
-          const float y1 = fmaf((hi_bf16(xr[i]) - mean) * rstd, s_gamma[c0 + 2 * i + 1], s_beta[c0 + 2 * i + 1]);
-          yb[ks][i] = pack_bf16(y0, y1);
+          const float h0 = (lo_bf16(xr[ks][i]) - mean) * rstd, h1 = (hi_bf16(xr[ks][i]) - mean) * rstd;
+          xh[i] = pack_bf16(h0, h1);
+          yb[ks][i] = pack_bf16(fmaf(lo_bf16(xh[i]), s_gamma[c0 + 2 * i], s_beta[c0 + 2 * i]),
+                                fmaf(hi_bf16(xh[i]), s_gamma[c0 + 2 * i + 1], s_beta[c0 + 2 * i + 1]));
         }
+        xh_dst[2 * ks] = xh;
       }
     }
     // dout as the B operand of dh, channels in accumulator-row order:
@@ -278,13 +290,14 @@ struct WLayout {
 //     contraction index is the token, go to an exchange buffer;
 //   waves 4..7 (phase C, chunk s): the product tiles M_a += da^T xhat,
 //     M_b += db^T xhat, Mo += dout^T h over the chunk's 64 tokens, then they stage
-//     chunk s + 2 (xhat normalised in registers, and dout), loaded one step
+//     chunk s + 2 (xhat rows written by the dx pass, and dout), loaded one step
 //     earlier so that the loads overlap a barrier and a phase C.
 // Three stages and two exchange buffers: one barrier per step.
 template <int KS>
 __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem p, TransBwdArgs a, int ngroups,
-                                                                   int ranges, int range_chunks, float* ma, float* mb,
-                                                                   float* mo, float* sa, float* sb) {
+                                                                   int ranges, int range_chunks, const uint16_t* xh,
+                                                                   float* ma, float* mb, float* mo, float* sa,
+                                                                   float* sb) {
   using L = TransLayout<KS>;
   using W = WLayout<KS>;
   constexpr int C = L::C;
@@ -322,20 +335,16 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
   };
 
   // ---- staging (phase-C waves): chunk c's xhat and dout rows, in registers then LDS
-  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
   const uint16_t* dog = static_cast<const uint16_t*>(a.dout);
   const int ctid = tid - CTHREADS;
   u32x4 xr[NPC], dr[NPC];
-  float xm[NPC], xs[NPC];
   // Tokens past the range are loaded from its last token (no branch around the
   // loads) and staged as zeros.
   // Addresses are a uniform base (the chunk's first token) plus 32-bit lane offsets.
   auto stage_load = [&](int c) {
     const int64_t t0 = t_begin + static_cast<int64_t>(c) * kTC;
-    const char* xb = reinterpret_cast<const char*>(pipe::uniform_ptr(xg + t0 * C));
+    const char* xb = reinterpret_cast<const char*>(pipe::uniform_ptr(xh + t0 * C));
     const char* db = reinterpret_cast<const char*>(pipe::uniform_ptr(dog + t0 * C));
-    const char* mb = reinterpret_cast<const char*>(pipe::uniform_ptr(a.mean + t0));
-    const char* rb = reinterpret_cast<const char*>(pipe::uniform_ptr(a.rstd + t0));
     const int tmax = static_cast<int>(t_end - 1 - t0);
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
@@ -344,8 +353,6 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
       const uint32_t off = static_cast<uint32_t>(t * (2 * C) + 16 * jj);
       xr[i] = *reinterpret_cast<const u32x4*>(xb + off);
       dr[i] = *reinterpret_cast<const u32x4*>(db + off);
-      xm[i] = *reinterpret_cast<const float*>(mb + 4u * static_cast<uint32_t>(t));
-      xs[i] = *reinterpret_cast<const float*>(rb + 4u * static_cast<uint32_t>(t));
     }
   };
   auto stage_store = [&](int c) {
@@ -357,12 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void transition_bwd_wpart(TransProblem
       const int idx = ctid + i * CTHREADS;
       const int t = idx / XPL, jj = idx - (idx / XPL) * XPL;
       const bool in = t0 + t < t_end;
-      const float nm = -xm[i] * xs[i];  // xhat = x rstd - mean rstd
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o[e] = in ? pack_bf16(fmaf(lo_bf16(xr[i][e]), xs[i], nm), fmaf(hi_bf16(xr[i][e]), xs[i], nm)) : 0u;
-      *reinterpret_cast<u32x4*>(sx + t * PX + 16 * jj) = o;
+      *reinterpret_cast<u32x4*>(sx + t * PX + 16 * jj) = in ? xr[i] : u32x4{0, 0, 0, 0};
       *reinterpret_cast<u32x4*>(sd + t * PX + 16 * jj) = in ? dr[i] : u32x4{0, 0, 0, 0};
     }
   };
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(kFinThreads) void transition_fin_cols(TransProblem 
 
 struct TWs {
   int ranges, range_chunks;
-  size_t ma, mb, mo, sa, sb, tg, tb, total;
+  size_t ma, mb, mo, sa, sb, tg, tb, xh, total;
 };
 
 TWs tws(const TransProblem& p) {
@@ -718,7 +720,10 @@ TWs tws(const TransProblem& p) {
   w.sb = up(w.sa + r * h);
   w.tg = up(w.sb + r * h);
   w.tb = up(w.tg + hc);
-  w.total = up(w.tb + hc);
+  w.xh = up(w.tb + hc);
+  // xhat rows for every token slot of the dx kernel's passes (kWaves x 32 tokens each)
+  const size_t slots = static_cast<size_t>((p.tiles + kWaves - 1) / kWaves) * kWaves * 32;
+  w.total = up(w.xh + slots * p.C * sizeof(uint16_t));
   return w;
 }
 
@@ -745,7 +750,8 @@ hipError_t launch_bwd(const TransProblem& p, const TransBwdArgs& a, char* ws, hi
     int grid = 0;
     if ((e = grid_for(transition_bwd_dx<KS>, lds, (p.tiles + kWaves - 1) / kWaves, &grid)) != hipSuccess) return e;
     KernelTimer timer("transition_bwd_dx", s);
-    hipLaunchKernelGGL(transition_bwd_dx<KS>, dim3(grid), dim3(kThreads), lds, s, p, a);
+    hipLaunchKernelGGL(transition_bwd_dx<KS>, dim3(grid), dim3(kThreads), lds, s, p, a,
+                       reinterpret_cast<uint16_t*>(ws + w.xh));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
@@ -756,7 +762,8 @@ hipError_t launch_bwd(const TransProblem& p, const TransBwdArgs& a, char* ws, hi
     const int ngroups = p.hidden / kHC;
     KernelTimer timer("transition_bwd_wpart", s);
     hipLaunchKernelGGL(transition_bwd_wpart<KS>, dim3(ngroups * w.ranges), dim3(kThreads), lds, s, p, a, ngroups,
-                       w.ranges, w.range_chunks, reinterpret_cast<float*>(ws + w.ma),
+                       w.ranges, w.range_chunks, reinterpret_cast<const uint16_t*>(ws + w.xh),
+                       reinterpret_cast<float*>(ws + w.ma),
                        reinterpret_cast<float*>(ws + w.mb), reinterpret_cast<float*>(ws + w.mo),
                        reinterpret_cast<float*>(ws + w.sa), reinterpret_cast<float*>(ws + w.sb));
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -119,8 +119,10 @@ evoattn_status_t evoattn_transition_fwd(int64_t a, int64_t b, int64_t channels, 
                                         float* mean, float* rstd, void* stream);
 
 /* Bytes of workspace evoattn_transition_bwd needs (fixed-order partial sums of the
- * weight gradients over at most 64 token ranges: O(ranges * n*C * C)).  Returns
- * 0 and records an error detail if the problem is invalid or unsupported. */
+ * weight gradients over at most 64 token ranges: O(ranges * n*C * C), plus the
+ * normalised input xhat in bf16, a*b*C*2 bytes, written by the dx pass and read by
+ * the weight-gradient pass).  Returns 0 and records an error detail if the
+ * problem is invalid or unsupported. */
 size_t evoattn_transition_bwd_workspace_bytes(int64_t a, int64_t b, int64_t channels, int64_t expansion,
                                               int dtype);
 
@@ -129,7 +131,8 @@ size_t evoattn_transition_bwd_workspace_bytes(int64_t a, int64_t b, int64_t chan
  * Outputs: dx (bf16), dgamma, dbeta (fp32 [C]), dw_a, dw_b (fp32 [n*C, C]),
  * dw_out (fp32 [C, n*C]).  a, b and h are recomputed on chip, never stored; the
  * sums over tokens run in a fixed order (bit-identical across calls).  da, db,
- * h, y and xhat are rounded to bf16 as matrix-core operands; sums are fp32. */
+ * h, y and xhat are rounded to bf16 as matrix-core operands (the backward forms y
+ * from the rounded xhat); sums are fp32. */
 evoattn_status_t evoattn_transition_bwd(int64_t a, int64_t b, int64_t channels, int64_t expansion, int dtype,
                                         const void* x, const float* gamma, const float* beta,
                                         const void* w_a, const void* w_b, const void* w_out,

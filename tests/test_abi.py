@@ -321,9 +321,12 @@ def test_transition_workspace_query():
     lib = _lib.load()
     n = lib.evoattn_transition_bwd_workspace_bytes(384, 384, 128, 4, 1)
     assert n % 256 == 0
-    # partial sums over at most 64 ranges of three n*C x C arrays, two n*C vectors, two n*C x C products
+    # partial sums over at most 64 ranges of three n*C x C arrays, two n*C vectors, two n*C x C products,
+    # and the normalised input rows in bf16
     hc = 512 * 128 * 4
-    assert n <= 64 * (3 * hc + 2 * 512 * 4) + 2 * hc + 8 * 256
+    xh = 384 * 384 * 128 * 2
+    assert n >= xh
+    assert n <= 64 * (3 * hc + 2 * 512 * 4) + 2 * hc + xh + 9 * 256
     assert lib.evoattn_transition_bwd_workspace_bytes(384, 384, 128, 4, 0) == 0   # fp32: unsupported
 
 

@@ -184,6 +184,28 @@ def test_bwd_shapes(A, B, C, n):
     check_bwd(generate_transition(A, B, C, n, dtype=torch.bfloat16, seed=A * 7 + n))
 
 
+@pytest.mark.parametrize("A,B,C", [(7, 9, 128), (33, 20, 64)])
+def test_bwd_ignores_workspace_contents(A, B, C):
+    """The workspace (partial sums, and the bf16 xhat rows the dx kernel hands to
+    the weight-gradient kernel, in whole 256-token passes) may hold anything on
+    entry: a workspace of NaN bytes gives the same bits as a zeroed one."""
+    import af3_attention_amd as ea
+    banner(f"bwd workspace contents A={A} B={B} C={C}")
+    inp = generate_transition(A, B, C, 4, dtype=torch.bfloat16, seed=A + B)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    fw = ea.transition_fwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"], eps=inp["eps"])
+    nbytes = ea.transition_bwd_workspace_bytes(A, B, C, 4)
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        outs.append(ea.transition_bwd(g["x"], g["gamma"], g["beta"], g["w_a"], g["w_b"], g["w_out"], fw["mean"],
+                                      fw["rstd"], g["dout"], workspace=ws))
+    torch.cuda.synchronize()
+    for n in outs[0]:
+        assert bool(torch.isfinite(outs[1][n]).all()), f"{n}: non-finite with a NaN-filled workspace"
+        assert torch.equal(outs[0][n], outs[1][n]), f"{n}: depends on the workspace contents"
+
+
 @pytest.mark.parametrize("name", ["pair_transition_bf16_n384", "msa_transition_bf16_s512_n384"])
 def test_bwd_workloads_sampled(name):
     """Full sizes in the benchmark's launch configuration with dout zero outside a

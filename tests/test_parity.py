@@ -47,6 +47,30 @@ def test_bf16_ragged_triangle(R, N, H, D, transpose):
     compare(gpu_fwd_bwd(inp), oracle_fwd_bwd(inp), "bf16", transpose)
 
 
+@pytest.mark.parametrize("transpose", [0, 1])
+def test_bwd_ignores_workspace_contents(transpose):
+    """The backward's workspace (tiled bias copies, per-row operands, dBias partial
+    sums) may hold anything on entry: a workspace of NaN bytes gives the same bits
+    as a zeroed one."""
+    import af3_attention_amd as ea
+    R, N, H, D = 17, 200, 4, 32
+    banner(f"bwd workspace contents R={R} N={N} t={transpose}")
+    inp = generate(R, N, H, D, dtype=torch.bfloat16, transpose=transpose, bias_std=math.sqrt(2),
+                   mask_kind="tail_uniform", mask_frac=0.15, seed=5)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    o, lse = ea.evoattn_fwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], bool(transpose))
+    nbytes = ea.evoattn_bwd_workspace_bytes(R, N, H, D)
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        outs.append(ea.evoattn_bwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], o, lse, g["dout"],
+                                   bool(transpose), workspace=ws))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dbias"), *outs):
+        assert bool(torch.isfinite(b).all()), f"{name}: non-finite with a NaN-filled workspace"
+        assert torch.equal(a, b), f"{name}: depends on the workspace contents"
+
+
 @pytest.mark.parametrize("R,N,H,D", [(40, 72, 8, 8), (21, 150, 8, 8), (12, 96, 4, 16), (10, 80, 2, 64)])
 def test_bf16_msa_like_and_other_dims(R, N, H, D):
     banner(f"bf16 msa-like R={R} N={N} H={H} D={D}")

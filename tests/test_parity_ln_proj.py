@@ -308,6 +308,31 @@ def test_bwd_bf16_shapes(A, B, C, H, D, qkv, bias, bt):
     check_bwd(generate_proj(A, B, C, H, D, dtype=torch.bfloat16, qkv=qkv, bias=bias, seed=A + C), bt, "bf16")
 
 
+@pytest.mark.parametrize("A,B,C,H,D,bt", [(37, 37, 64, 8, 8, 0), (29, 29, 128, 2, 64, 1)])
+def test_bwd_ignores_workspace_contents(A, B, C, H, D, bt):
+    """The workspace (fixed-order partial sums) may hold anything on entry: a
+    workspace of NaN bytes gives the same bits as a zeroed one."""
+    import af3_attention_amd as ea
+    banner(f"bwd workspace contents A={A} B={B} C={C} H={H} D={D} bt={bt}")
+    inp = generate_proj(A, B, C, H, D, dtype=torch.bfloat16, qkv=True, bias=True, seed=A * 3 + C)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    fw = ea.ln_proj_fwd(g["x"], g["gamma"], g["beta"], g["w_qkv"], g["w_bias"], heads=H, head_dim=D,
+                        bias_transpose=bt, eps=inp["eps"])
+    nbytes = ea.ln_proj_bwd_workspace_bytes(A, B, C, H, D)
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        outs.append(ea.ln_proj_bwd(g["x"], g["gamma"], g["beta"], g["w_qkv"], g["w_bias"], fw["mean"], fw["rstd"],
+                                   g["dq"], g["dk"], g["dv"], g["dbias"], heads=H, head_dim=D, bias_transpose=bt,
+                                   workspace=ws))
+    torch.cuda.synchronize()
+    for n in outs[0]:
+        if outs[0][n] is None:
+            continue
+        assert bool(torch.isfinite(outs[1][n]).all()), f"{n}: non-finite with a NaN-filled workspace"
+        assert torch.equal(outs[0][n], outs[1][n]), f"{n}: depends on the workspace contents"
+
+
 @pytest.mark.parametrize("mode", ["fp32", "bf16"])
 @pytest.mark.parametrize("A,C,H,D,bt", [(20, 96, 2, 16, 1), (9, 256, 4, 32, 0)])
 def test_bwd_vector_kernel_shapes(A, C, H, D, bt, mode):

@@ -8,17 +8,14 @@
 namespace evo {
 namespace {
 
-// Tiled layout (see pipe_common.h).  One workgroup per 32 x 32 block (query tile
-// qt, key tile kt) of one head: the block is read once (coalesced rows of 32 keys)
-// into LDS, then written in the query-lane order to out_q and, if out_k is not
-// NULL, in the key-lane order to out_k, each as 256 coalesced 16-byte stores.
+// One 32 x 32 bias tile (query tile qt, key tile kt) of head h.
 template <typename T>
-__global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __restrict__ bias, float* __restrict__ out_q,
-                                                         float* __restrict__ out_k, int nt) {
-  __shared__ float tile[32][33];  // [query][key], padded
-  const int kt = blockIdx.x % nt;
-  const int qt = (blockIdx.x / nt) % nt;
-  const int h = blockIdx.x / (nt * nt);
+__device__ __forceinline__ void bias_tile(const Problem& p, const T* __restrict__ bias, float* __restrict__ out_q,
+                                          float* __restrict__ out_k, int nt, int tile) {
+  __shared__ float tile_lds[32][33];  // [query][key], padded
+  const int kt = tile % nt;
+  const int qt = (tile / nt) % nt;
+  const int h = tile / (nt * nt);
   const float sd = sqrtf(static_cast<float>(p.D));
   const int t = threadIdx.x;
 #pragma unroll
@@ -33,7 +30,7 @@ __global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __r
     } else {
       val = sd * Elem<T>::load(bias, (static_cast<int64_t>(h) * p.N + j) * p.N + k);
     }
-    tile[jj][kk] = val;
+    tile_lds[jj][kk] = val;
   }
   __syncthreads();
   // Thread t writes floats 4t..4t+3 of the tile: register group g = t / 64 of lane
@@ -43,10 +40,53 @@ __global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __r
   const int64_t off = (((static_cast<int64_t>(h) * nt + qt) * nt + kt) * 1024) + 4 * t;
   // Query lanes: rows are keys, the column is the query.
   *reinterpret_cast<float4*>(out_q + off) =
-      make_float4(tile[col][row0], tile[col][row0 + 1], tile[col][row0 + 2], tile[col][row0 + 3]);
+      make_float4(tile_lds[col][row0], tile_lds[col][row0 + 1], tile_lds[col][row0 + 2], tile_lds[col][row0 + 3]);
   if (out_k)  // key lanes: rows are queries, the column is the key
     *reinterpret_cast<float4*>(out_k + off) =
-        make_float4(tile[row0][col], tile[row0 + 1][col], tile[row0 + 2][col], tile[row0 + 3][col]);
+        make_float4(tile_lds[row0][col], tile_lds[row0 + 1][col], tile_lds[row0 + 2][col], tile_lds[row0 + 3][col]);
+}
+
+// Tiled layout (see pipe_common.h).  One workgroup per 32 x 32 block (query tile
+// qt, key tile kt) of one head: the block is read once (coalesced rows of 32 keys)
+// into LDS, then written in the query-lane order to out_q and, if out_k is not
+// NULL, in the key-lane order to out_k, each as 256 coalesced 16-byte stores.
+template <typename T>
+__global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __restrict__ bias, float* __restrict__ out_q,
+                                                         float* __restrict__ out_k, int nt) {
+  bias_tile(p, bias, out_q, out_k, nt, blockIdx.x);
+}
+
+// Forward pre-pass: the bias tiles in the query-lane order (blocks 0 .. tiles - 1)
+// and, with a mask, one block per attention row r: the key-side split operand of
+// sqrt(d) * mask[r][k] for every key (pipe::key_aug's layout in all 16 bytes,
+// with a masked key's -inf kept exact) and the last key of the row that is not
+// masked (-1 if there is none).
+template <typename T>
+__global__ __launch_bounds__(256) void fwd_prep_kernel(Problem p, const T* __restrict__ bias, const float* __restrict__ mask,
+                                                       float* __restrict__ out_q, uint4* __restrict__ kaug,
+                                                       int* __restrict__ last_live, int nt, int tiles) {
+  if (static_cast<int>(blockIdx.x) < tiles) {
+    bias_tile(p, bias, out_q, static_cast<float*>(nullptr), nt, blockIdx.x);
+    return;
+  }
+  __shared__ int red[4];
+  const int r = blockIdx.x - tiles;
+  const float sd = sqrtf(static_cast<float>(p.D));
+  int last = -1;
+  for (int k = threadIdx.x; k < p.N; k += 256) {
+    const float m = mask[static_cast<int64_t>(r) * p.N + k];
+    const float ms = sd * m;
+    // A masked key carries -inf itself (one bf16 part; the others 0), so its
+    // logit is exactly -inf.
+    const pipe::Split3 sm = ms == -INFINITY ? pipe::Split3{0xff80u, 0u, 0u} : pipe::split3(ms);
+    kaug[static_cast<int64_t>(r) * p.N + k] =
+        make_uint4(pipe::kBf16One | (pipe::kBf16One << 16), pipe::kBf16One | (sm.hi << 16), sm.mid | (sm.lo << 16), 0u);
+    if (m != -INFINITY) last = k;
+  }
+  for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = last;
+  __syncthreads();
+  if (threadIdx.x == 0) last_live[r] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
 }  // namespace
@@ -62,6 +102,17 @@ hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out_q, f
   KernelTimer timer(out_k ? "bias_tiles_qk" : "bias_tiles_q", s);
   hipLaunchKernelGGL((bias_tiles_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p,
                      static_cast<const uint16_t*>(bias), out_q, out_k, nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_prep(const Problem& p, const void* bias, const float* mask, float* out_q, void* kaug,
+                           int* last_live, hipStream_t s) {
+  const int nt = bias_tiles(p.N);
+  const int tiles = p.H * nt * nt;
+  const int64_t blocks = static_cast<int64_t>(tiles) + (mask ? p.R : 0);
+  KernelTimer timer("fwd_prep", s);
+  hipLaunchKernelGGL((fwd_prep_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p,
+                     static_cast<const uint16_t*>(bias), mask, out_q, static_cast<uint4*>(kaug), last_live, nt, tiles);
   return hipGetLastError();
 }
 

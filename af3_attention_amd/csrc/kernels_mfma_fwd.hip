@@ -1,4 +1,5 @@
-// bf16 MFMA forward of pair-biased 3D attention for gfx950.
+// bf16 MFMA forward of pair-biased 3D attention for gfx950, head_dim 64 (head_dim
+// 8, 16 and 32 run the ping-pong kernel in kernels_fwd_pp.hip).
 //
 // The MegaFold pages (gist.science technical summary, Methodik section 1
 // "EvoFlash-3D") describe the method: logits of a row are produced tile by tile
@@ -17,8 +18,8 @@
 //    plus one exchange with lane l ^ 32;
 //  * the softmax keeps a lazily refreshed reference point (the exponentials of a
 //    block may exceed 1 until a lane's block sum crosses a bound), so a block
-//    normally costs one FMA, one exp2, half a pack and half a dot2 per logit and
-//    no max reduction or rescale;
+//    normally costs one FMA, one exp2, half a pack and one add per logit (the
+//    normaliser sums the fp32 probabilities) and no max reduction or rescale;
 //  * the MFMA accumulator starts from sqrt(d) * bias, read as four coalesced 1 KB
 //    loads from a pre-pass's tiled copy, so the bias costs no vector ALU work;
 //    one FMA per logit applies log2(e)/sqrt(d) and subtracts the running max;
@@ -251,25 +252,22 @@ __global__ __launch_bounds__(256, 2) void fwd_pipe_kernel(Problem p, FwdArgs a, 
         u32x4 pb[2][2];  // P^T packed to bf16: [key tile][16-key half]
         float lsum;
         auto exponentiate = [&](float m_use) {
+          // The normaliser sums the fp32 probabilities (four independent chains).
+          float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               float pv[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[i][mb][8 * t + e], c1, -m_use));
+              for (int e = 0; e < 8; ++e) {
+                pv[e] = fast_exp2(__builtin_fmaf(s[i][mb][8 * t + e], c1, -m_use));
+                ls[e & 3] += pv[e];
+              }
               pb[mb][t] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
                                 pack_bf16(pv[6], pv[7])};
             }
           }
-          // Sum of the bf16 probabilities that enter P V (four independent chains).
-          float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) ls[e] = add_bf16_pair(pb[mb][t][e], ls[e]);
           lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
         };
         const bool fresh = __ballot(m_run[i] == -INFINITY) != 0;
@@ -333,14 +331,28 @@ hipError_t fwd_pipe_dispatch(const Problem& p, const FwdArgs& a, float* bias_t, 
 
 }  // namespace
 
-size_t fwd_mfma_workspace_bytes(const Problem& p) { return tiled_bias_bytes(p); }
+namespace {
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+// Workspace: tiled bias | (head_dim <= 32) per-key mask operands [R,N] x 16 B |
+// last live key of each row [R] x 4 B.
+size_t fwd_mfma_workspace_bytes(const Problem& p) {
+  size_t b = align256(tiled_bias_bytes(p));
+  if (p.D <= 32) b += align256(static_cast<size_t>(p.R) * p.N * 16) + align256(static_cast<size_t>(p.R) * 4);
+  return b;
+}
 
 hipError_t launch_fwd_mfma(const Problem& p, const FwdArgs& a, void* ws, hipStream_t s) {
   float* bias_t = static_cast<float*>(ws);
+  if (p.D <= 32) {
+    char* kaug = static_cast<char*>(ws) + align256(tiled_bias_bytes(p));
+    int* last_live = reinterpret_cast<int*>(kaug + align256(static_cast<size_t>(p.R) * p.N * 16));
+    return launch_fwd_pp(p, a, bias_t, kaug, last_live, s);
+  }
   switch (p.D) {
-    case 8: return fwd_pipe_dispatch<8>(p, a, bias_t, s);
-    case 16: return fwd_pipe_dispatch<16>(p, a, bias_t, s);
-    case 32: return fwd_pipe_dispatch<32>(p, a, bias_t, s);
     case 64: return fwd_pipe_dispatch<64>(p, a, bias_t, s);
     default: return hipErrorInvalidValue;
   }

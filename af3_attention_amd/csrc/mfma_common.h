@@ -59,12 +59,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // an asm read of a fresh MFMA result could miss the required wait states.)
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// acc + lo(p) + hi(p) for a packed bf16 pair p, in one v_dot2_f32_bf16 with (1, 1).
-__device__ __forceinline__ float add_bf16_pair(uint32_t p, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
-                                         false);
-}
-
 __device__ __forceinline__ int64_t elem_offset(const Problem& p, int r, int pos, int h) {
   return ((static_cast<int64_t>(r) * p.row_stride + static_cast<int64_t>(pos) * p.pos_stride) * p.H + h) * p.D;
 }

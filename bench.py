@@ -58,7 +58,7 @@ CSRC = os.path.join(HERE, "af3_attention_amd", "csrc")
 # while these are unchanged since its counters were taken.
 COMMON_SOURCES = ["evoattn_internal.h", "mfma_common.h", "pipe_common.h"]
 KERNEL_SOURCES = {
-    "fwd_mfma": ["kernels_mfma_fwd.hip"],
+    "fwd_mfma": ["kernels_mfma_fwd.hip", "kernels_fwd_pp.hip", "kernels_bias_prep.hip", "dma_common.h"],
     "bwd_dkdv_mfma": ["kernels_bwd_dkdv.hip"],
     "bwd_dq_mfma": ["kernels_bwd_dq.hip"],
     "bwd_dbias_mfma": ["kernels_bwd_dbias.hip"],

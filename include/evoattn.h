@@ -96,7 +96,9 @@ const char* evoattn_status_string(int status);
 /* Description of the last failed call on the calling thread ("" if none). */
 const char* evoattn_last_error_detail(void);
 
-/* Bytes of workspace evoattn_fwd needs for this problem (may be 0).
+/* Bytes of workspace evoattn_fwd needs for this problem (may be 0): for bf16
+ * the sqrt(d)-scaled bias as fp32 tiles (O(H*N*N)) and, for head_dim <= 32, the
+ * key-side mask operands and each row's last unmasked key (O(R*N)).
  * Returns 0 and records an error detail if the problem is invalid. */
 size_t evoattn_fwd_workspace_bytes(int64_t rows, int64_t n, int64_t heads,
                                    int64_t head_dim, int dtype);

@@ -5,12 +5,9 @@ Tolerances (from the statement of the target for this operator):
   fp32 mode: every output within 1e-4 max abs of the fp64 oracle.
   bf16 mode: O within 2e-2 max abs; each gradient within 5e-2 of the oracle,
              measured as max|g - g_ref| / max|g_ref| ("relative to max norm");
-             lse within 4e-3 max abs.  The softmax normaliser is the sum of
-             the bf16-rounded probabilities that also weight V (so O is an exact
-             convex combination of V rows).  Round-to-nearest-even to bf16 (8
-             significant bits) has relative error at most 2^-8, so the sum, and
-             hence exp(lse), is off by a factor within 1 +- 2^-8:
-             |lse - lse_exact| <= 2^-8 (3.9e-3) plus fp32 noise.
+             lse within 1e-3 max abs (a tolerance the statement leaves open; the
+             kernels sum the fp32 probabilities, so lse carries only fp32
+             rounding of the logits and the sum).
 """
 import numpy as np
 import torch
@@ -20,7 +17,7 @@ import oracle
 FP32_ATOL = 1e-4
 BF16_O_ATOL = 2e-2
 BF16_GRAD_REL = 5e-2
-BF16_LSE_ATOL = 4e-3
+BF16_LSE_ATOL = 1e-3
 
 
 def to_np(t):

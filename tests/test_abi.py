@@ -56,7 +56,9 @@ def test_workspace_queries():
     lib = _lib.load()
     fws = lib.evoattn_fwd_workspace_bytes(384, 384, 4, 32, 1)
     assert fws % 256 == 0
-    assert fws <= 4 * 512 * 512 * 4          # one padded fp32 copy of the bias at most
+    # one padded fp32 copy of the bias, 16 bytes per (row, key) of mask operands
+    # and one int per row (each rounded up to 256 bytes) at most
+    assert fws <= 4 * 512 * 512 * 4 + 384 * 384 * 16 + 384 * 4 + 3 * 256
     assert lib.evoattn_fwd_workspace_bytes(64, 64, 4, 32, 0) == 0   # fp32 path needs none
     ws = lib.evoattn_bwd_workspace_bytes(384, 384, 4, 32, 1)
     assert ws >= 384 * 4 * 384 * 4            # at least the per-row statistics

@@ -9,6 +9,7 @@ from .evoattn import (  # noqa: F401
     evoattn_bwd,
     evoattn_bwd_workspace_bytes,
     evoattn_fwd,
+    evoattn_fwd_noalloc,
     evoattn_fwd_workspace_bytes,
 )
 from ._lib import EvoAttnError, LIB_PATH  # noqa: F401

@@ -13,6 +13,7 @@ EXPORTS = (
     "evoattn_fwd_workspace_bytes",
     "evoattn_bwd_workspace_bytes",
     "evoattn_fwd",
+    "evoattn_fwd_noalloc",
     "evoattn_bwd",
     "evoattn_timing_enable",
     "evoattn_timing_collect",
@@ -52,6 +53,9 @@ def load():
     lib.evoattn_fwd.argtypes = [i64, i64, i64, i64, c_int, c_int,
                                 vp, vp, vp, vp, fp, vp, fp, vp, sz, vp]
     lib.evoattn_fwd.restype = c_int
+    lib.evoattn_fwd_noalloc.argtypes = [i64, i64, i64, i64, c_int, c_int,
+                                        vp, vp, vp, vp, fp, vp, fp, vp]
+    lib.evoattn_fwd_noalloc.restype = c_int
     lib.evoattn_bwd.argtypes = [i64, i64, i64, i64, c_int, c_int,
                                 vp, vp, vp, vp, fp, vp, fp, vp, vp, vp, vp, fp, vp, sz, vp]
     lib.evoattn_bwd.restype = c_int

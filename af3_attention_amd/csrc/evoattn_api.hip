@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "evoattn.h"
@@ -166,6 +167,38 @@ evoattn_status_t check_transition(int64_t A, int64_t B, int64_t C, int64_t expan
   return EVOATTN_OK;
 }
 
+// Scratch of evoattn_fwd_noalloc: a file-scope device array, so that the entry
+// point needs no allocation.  Every device that runs the library holds its own
+// copy until the process ends.  In host code `scratch` only names the symbol;
+// its device address (one per device) comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = EVOATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept.
+evoattn_status_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(EVOATTN_ERR_DEVICE, "device index %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(EVOATTN_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return EVOATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,6 +256,25 @@ evoattn_status_t evoattn_fwd(int64_t rows, int64_t n, int64_t heads, int64_t hea
   if (e != hipSuccess) return fail(EVOATTN_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return EVOATTN_OK;
+}
+
+evoattn_status_t evoattn_fwd_noalloc(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype,
+                                     int transpose, const void* q, const void* k, const void* v, const void* bias,
+                                     const float* mask, void* o, float* lse, void* stream) {
+  evo::Problem p;
+  evoattn_status_t st = check_problem(rows, n, heads, head_dim, dtype, transpose, &p);
+  if (st != EVOATTN_OK) return st;
+  const size_t need = fwd_ws_bytes(p);
+  if (need > kNoAllocScratchBytes)
+    return fail(EVOATTN_ERR_WORKSPACE,
+                "problem needs %zu bytes of scratch; evoattn_fwd_noalloc holds at most %zu "
+                "(EVOATTN_NOALLOC_SCRATCH_BYTES): call evoattn_fwd with a workspace instead",
+                need, kNoAllocScratchBytes);
+  if ((st = check_device()) != EVOATTN_OK) return st;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != EVOATTN_OK) return st;
+  return evoattn_fwd(rows, n, heads, head_dim, dtype, transpose, q, k, v, bias, mask, o, lse, ws,
+                     kNoAllocScratchBytes, stream);
 }
 
 evoattn_status_t evoattn_bwd(int64_t rows, int64_t n, int64_t heads, int64_t head_dim, int dtype, int transpose,

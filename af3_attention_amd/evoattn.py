@@ -83,6 +83,30 @@ def evoattn_fwd(q, k, v, bias=None, mask=None, transpose=False, need_lse=True, o
     return o, lse
 
 
+def evoattn_fwd_noalloc(q, k, v, bias=None, mask=None, transpose=False, out=None, lse_out=None):
+    """Forward through the entry point that allocates nothing (its scratch is a static
+    device array of the library).  Pass `out` and `lse_out` to allocate nothing here
+    either; otherwise they are created.  Returns (o, lse)."""
+    lib = _lib.load()
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    R, N, H, D = _dims(q, transpose)
+    dev = q.device
+    _check(q, "q", q.shape, q.dtype, dev)
+    _check(k, "k", q.shape, q.dtype, dev)
+    _check(v, "v", q.shape, q.dtype, dev)
+    _check(bias, "bias", (H, N, N), q.dtype, dev, optional=True)
+    _check(mask, "mask", (R, N), torch.float32, dev, optional=True)
+    o = out if out is not None else torch.empty_like(q)
+    _check(o, "out", q.shape, q.dtype, dev)
+    lse = lse_out if lse_out is not None else torch.empty((R, H, N), dtype=torch.float32, device=dev)
+    _check(lse, "lse_out", (R, H, N), torch.float32, dev)
+    st = lib.evoattn_fwd_noalloc(R, N, H, D, _DTYPES[q.dtype], int(bool(transpose)),
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(o), _ptr(lse), _stream(dev))
+    _lib.check(st, "evoattn_fwd_noalloc")
+    return o, lse
+
+
 def evoattn_bwd(q, k, v, bias, mask, o, lse, dout, transpose=False, need_dbias=True, workspace=None):
     """Backward of sum(o * dout).  Returns (dq, dk, dv, dbias); dbias is fp32 [H,N,N] or None."""
     lib = _lib.load()

@@ -118,6 +118,23 @@ evoattn_status_t evoattn_fwd(int64_t rows, int64_t n, int64_t heads, int64_t hea
                              void* o, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward without allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as evoattn_fwd, minus the workspace:
+ * the library uses a static device array of EVOATTN_NOALLOC_SCRATCH_BYTES per
+ * device instead (held until the process ends; no hipMalloc/hipFree or other
+ * allocating call is made).  Returns EVOATTN_ERR_WORKSPACE when the problem needs
+ * more scratch than that (evoattn_fwd_workspace_bytes tells).  Every call on a
+ * device shares that device's array: calls that overlap in time on one device
+ * (different streams or threads) race on it and must be serialised by the
+ * caller.  Nothing in the array needs to start at zero. */
+#define EVOATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+evoattn_status_t evoattn_fwd_noalloc(int64_t rows, int64_t n, int64_t heads, int64_t head_dim,
+                                     int dtype, int transpose,
+                                     const void* q, const void* k, const void* v,
+                                     const void* bias, const float* mask,
+                                     void* o, float* lse, void* stream);
+
 /* Backward of sum(o * dout).  Inputs: the forward's inputs, its outputs o and
  * lse (required), and dout (dtype, layout of o).  Outputs dq, dk, dv (dtype,
  * layout of q) and dbias [H,N,N] fp32 (NULL to skip).  The mask receives no

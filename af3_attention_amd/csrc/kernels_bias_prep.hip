@@ -38,9 +38,9 @@ __device__ __forceinline__ void bias_tile(const Problem& p, const T* __restrict_
   const int g = t >> 6, lane = t & 63;
   const int row0 = 8 * g + 4 * (lane >> 5), col = lane & 31;
   const int64_t off = (((static_cast<int64_t>(h) * nt + qt) * nt + kt) * 1024) + 4 * t;
-  // Query lanes: rows are keys, the column is the query.
-  *reinterpret_cast<float4*>(out_q + off) =
-      make_float4(tile_lds[col][row0], tile_lds[col][row0 + 1], tile_lds[col][row0 + 2], tile_lds[col][row0 + 3]);
+  if (out_q)  // query lanes: rows are keys, the column is the query
+    *reinterpret_cast<float4*>(out_q + off) =
+        make_float4(tile_lds[col][row0], tile_lds[col][row0 + 1], tile_lds[col][row0 + 2], tile_lds[col][row0 + 3]);
   if (out_k)  // key lanes: rows are queries, the column is the key
     *reinterpret_cast<float4*>(out_k + off) =
         make_float4(tile_lds[row0][col], tile_lds[row0 + 1][col], tile_lds[row0 + 2][col], tile_lds[row0 + 3][col]);
@@ -48,8 +48,8 @@ __device__ __forceinline__ void bias_tile(const Problem& p, const T* __restrict_
 
 // Tiled layout (see pipe_common.h).  One workgroup per 32 x 32 block (query tile
 // qt, key tile kt) of one head: the block is read once (coalesced rows of 32 keys)
-// into LDS, then written in the query-lane order to out_q and, if out_k is not
-// NULL, in the key-lane order to out_k, each as 256 coalesced 16-byte stores.
+// into LDS, then written in the query-lane order to out_q and in the key-lane
+// order to out_k (each skipped when NULL), each as 256 coalesced 16-byte stores.
 template <typename T>
 __global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __restrict__ bias, float* __restrict__ out_q,
                                                          float* __restrict__ out_k, int nt) {
@@ -99,7 +99,7 @@ size_t tiled_bias_bytes(const Problem& p) {
 hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out_q, float* out_k, hipStream_t s) {
   const int nt = bias_tiles(p.N);
   const int64_t blocks = static_cast<int64_t>(p.H) * nt * nt;
-  KernelTimer timer(out_k ? "bias_tiles_qk" : "bias_tiles_q", s);
+  KernelTimer timer(out_q ? (out_k ? "bias_tiles_qk" : "bias_tiles_q") : "bias_tiles_k", s);
   hipLaunchKernelGGL((bias_tiles_kernel<uint16_t>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p,
                      static_cast<const uint16_t*>(bias), out_q, out_k, nt);
   return hipGetLastError();

@@ -8,10 +8,14 @@
 // D[j] = sum_c dO[j,c] O[j,c], the gradients are
 //   dV = P^T dO,  dK = dS^T Q / sqrt(d),  dQ = dS K / sqrt(d),
 //   dBias[h,j,k] = sum over rows r of dS[r,h,j,k].
-// Three kernels each own complete outputs, so nothing is accumulated with
-// atomics and every sum has a fixed order:
-//  * dq   (kernels_bwd_dq.hip): a workgroup owns queries and walks the keys;
-//  * dkdv (kernels_bwd_dkdv.hip): a workgroup owns keys and walks the queries;
+// Every kernel owns complete outputs, so nothing is accumulated with atomics
+// and every sum has a fixed order:
+//  * fused (kernels_bwd_fused.hip), head_dim <= 32 and N <= 384: a workgroup owns
+//    one attention row of one head and forms its dQ, dK and dV from one pass over
+//    the score tiles;
+//  * otherwise dq (kernels_bwd_dq.hip), where a workgroup owns queries and walks
+//    the keys, and dkdv (kernels_bwd_dkdv.hip), where it owns keys and walks the
+//    queries;
 //  * dbias (kernels_bwd_dbias.hip): a workgroup owns a (query, key) tile of a
 //    head and walks a fixed group of rows; a last pass adds the groups' partial
 //    sums in increasing group order.
@@ -96,9 +100,14 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_q, 
                        s, p, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = launch_bias_tiles(p, a.bias, bias_q, bias_k, s)) != hipSuccess) return e;
-  if ((e = launch_dq_pipe(p, a, bias_q, s)) != hipSuccess) return e;
-  if ((e = launch_dkdv_pipe(p, a, bias_k, s)) != hipSuccess) return e;
+  if (bwd_fused_supported(p)) {
+    if ((e = launch_bias_tiles(p, a.bias, nullptr, bias_k, s)) != hipSuccess) return e;
+    if ((e = launch_bwd_fused(p, a, bias_k, s)) != hipSuccess) return e;
+  } else {
+    if ((e = launch_bias_tiles(p, a.bias, bias_q, bias_k, s)) != hipSuccess) return e;
+    if ((e = launch_dq_pipe(p, a, bias_q, s)) != hipSuccess) return e;
+    if ((e = launch_dkdv_pipe(p, a, bias_k, s)) != hipSuccess) return e;
+  }
   if (a.dbias) {
     float* target = groups == 1 ? a.dbias : dbias_part;
     if ((e = launch_dbias_pipe(p, a, bias_k, groups, target, s)) != hipSuccess) return e;

@@ -318,14 +318,18 @@ __device__ __forceinline__ f32x16 load_bias_tile(const float* __restrict__ tile,
 // Number of 32-wide tiles per axis of the tiled bias (positions padded to 128).
 inline int bias_tiles(int n) { return (n + 127) / 128 * 4; }
 size_t tiled_bias_bytes(const Problem& p);
-// Writes the tiled, sqrt(d)-scaled fp32 bias in the query-lane order to out_q and,
-// if out_k is not NULL, in the key-lane order to out_k (see above).
+// Writes the tiled, sqrt(d)-scaled fp32 bias in the query-lane order to out_q and
+// in the key-lane order to out_k (see above); either may be NULL.
 hipError_t launch_bias_tiles(const Problem& p, const void* bias, float* out_q, float* out_k, hipStream_t s);
 // Forward pre-pass: the tiled bias in the query-lane order and, if mask is not
 // NULL, the per-key split mask operands kaug [R,N] x 16 B and the last live key
 // of each row last_live [R] (kernels_bias_prep.hip).
 hipError_t launch_fwd_prep(const Problem& p, const void* bias, const float* mask, float* out_q, void* kaug,
                            int* last_live, hipStream_t s);
+// dQ, dK, dV in one pass (kernels_bwd_fused.hip), for head_dim <= 32 and N <= 384;
+// needs the per-row split operands (qaug, kaug) and the key-lane bias tiles.
+bool bwd_fused_supported(const Problem& p);
+hipError_t launch_bwd_fused(const Problem& p, const BwdArgs& a, const float* bias_k, hipStream_t s);
 // bf16 forward for head_dim 8, 16, 32 (kernels_fwd_pp.hip).
 hipError_t launch_fwd_pp(const Problem& p, const FwdArgs& a, float* bias_t, void* kaug, int* last_live,
                          hipStream_t s);

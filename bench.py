@@ -42,6 +42,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_FLOP_FACTOR = {
     "fwd_mfma": (4.0, "mfma"),
     "bwd_mfma": (10.0, "mfma"),
+    "bwd_fused_mfma": (10.0, "mfma"),
     "bwd_dkdv_mfma": (8.0, "mfma"),
     "bwd_dq_mfma": (6.0, "mfma"),
     "bwd_dbias_mfma": (4.0, "mfma"),
@@ -59,6 +60,7 @@ CSRC = os.path.join(HERE, "af3_attention_amd", "csrc")
 COMMON_SOURCES = ["evoattn_internal.h", "mfma_common.h", "pipe_common.h"]
 KERNEL_SOURCES = {
     "fwd_mfma": ["kernels_mfma_fwd.hip", "kernels_fwd_pp.hip", "kernels_bias_prep.hip", "dma_common.h"],
+    "bwd_fused_mfma": ["kernels_bwd_fused.hip"],
     "bwd_dkdv_mfma": ["kernels_bwd_dkdv.hip"],
     "bwd_dq_mfma": ["kernels_bwd_dq.hip"],
     "bwd_dbias_mfma": ["kernels_bwd_dbias.hip"],

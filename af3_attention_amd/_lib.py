@@ -4,7 +4,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libevoattn.so")
+# EVOATTN_LIB names another build of the library (the sanitizer build of the CPU
+# ABI tests); by default the one built in the package directory.
+LIB_PATH = os.environ.get("EVOATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libevoattn.so")
 
 EXPORTS = (
     "evoattn_abi_version",

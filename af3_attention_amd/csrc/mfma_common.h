@@ -81,7 +81,8 @@ __device__ __forceinline__ u32x4 global_operand(const Problem& p, const uint16_t
                                                 int half) {
   const int d0 = ks * 16 + 8 * half;
   if (pos >= p.N || d0 >= D) return u32x4{0u, 0u, 0u, 0u};
-  return *reinterpret_cast<const u32x4*>(src + elem_offset(p, r, pos, h) + d0);
+  typedef __attribute__((address_space(1))) const u32x4 gu32x4;  // a global (not flat) load
+  return *(gu32x4*)(src + elem_offset(p, r, pos, h) + d0);
 }
 
 // Store a transposed [d][pos] accumulator (lane = position) as bf16 into the

@@ -298,13 +298,17 @@ __device__ __forceinline__ int64_t bias_tile_offset(int h, int qt, int kt, int n
 
 __device__ __forceinline__ f32x16 load_bias_tile(const float* __restrict__ tile, int lane) {
   // The tile address is the same in every lane: as a scalar base plus a 32-bit
-  // lane offset the loads need no per-lane 64-bit address arithmetic.
-  const char* base = reinterpret_cast<const char*>(uniform_ptr(tile));
+  // lane offset the loads need no per-lane 64-bit address arithmetic.  The global
+  // address space keeps them global (not flat) loads, which count in vmcnt only,
+  // so waits for LDS reads do not also wait for them.
+  typedef __attribute__((address_space(1))) const char gchar;
+  typedef __attribute__((address_space(1))) const f32x4 gf32x4;
+  gchar* base = (gchar*)(uniform_ptr(tile));
   const uint32_t off = static_cast<uint32_t>(lane) * 16;
   f32x16 c;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(base + off + g * 1024);
+    const f32x4 x = *reinterpret_cast<gf32x4*>(base + off + g * 1024);
     c[4 * g + 0] = x[0];
     c[4 * g + 1] = x[1];
     c[4 * g + 2] = x[2];

@@ -194,8 +194,12 @@ def memory_curve():
 
     The library keeps O(R*H*N + H*N^2) bytes besides its inputs and outputs.  The
     reference forms the [R,H,N,N] scores, probabilities and their gradients in fp32
-    with torch autograd (fp32, because torch's bf16 batched products with transposed
-    operands are unsafe on this GPU) until it runs out of memory.
+    with torch autograd until it runs out of memory.  It runs in fp32 because the
+    backward of a bf16 batched product makes torch issue batched products whose
+    right operand is a transposed view, and those have faulted GPUs of this kind;
+    a bf16 reference would hold the same tensors at half the bytes.  The last record
+    is the long-sequence case run back to back: the starting-node and the
+    ending-node forward with both outputs and lse kept, then both backward passes.
     """
     import torch
     import af3_attention_amd as ea
@@ -241,9 +245,29 @@ def memory_curve():
         out.append(row)
         print(json.dumps(row), file=sys.stderr, flush=True)
         del g
+    # N = 1536, both variants back to back with both forward results live.
+    n = 1536
+    gs = []
+    for t in (0, 1):
+        inp = generate(n, n, 4, 32, dtype=torch.bfloat16, transpose=t, bias_std=2 ** 0.5, mask_kind="tail_fixed",
+                       mask_frac=0.05, seed=t)
+        gs.append({x: (None if inp[x] is None else inp[x].to(dev)) for x in ("q", "k", "v", "bias", "mask", "dout")})
+        del inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    fwd_out = [ea.evoattn_fwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], bool(t)) for t, g in enumerate(gs)]
+    grads = [ea.evoattn_bwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], o, lse, g["dout"], bool(t))
+             for t, (g, (o, lse)) in enumerate(zip(gs, fwd_out))]
+    torch.cuda.synchronize()
+    back_to_back = {"n": n, "rows": n, "variants": [0, 1], "inputs_bytes": base,
+                    "fused_peak_extra_bytes": torch.cuda.max_memory_allocated(dev) - base}
+    print(json.dumps(back_to_back), file=sys.stderr, flush=True)
+    del fwd_out, grads, gs
     total = torch.cuda.get_device_properties(dev).total_memory
-    print(json.dumps({"memory_curve": out, "device_memory_bytes": total, "dtype": "bf16",
-                      "config": {"heads": 4, "head_dim": 32, "mask": "tail 5%"}}), flush=True)
+    print(json.dumps({"memory_curve": out, "back_to_back_n1536": back_to_back, "device_memory_bytes": total,
+                      "dtype": "bf16", "config": {"heads": 4, "head_dim": 32, "mask": "tail 5%"}}), flush=True)
 
 
 def copy_calibration(dev):

@@ -27,7 +27,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "evo_oracle.c")
-_LIB = os.path.join(_HERE, "libevo_oracle.so")
+# EVO_ORACLE_SANITIZE=1 selects a build instrumented with AddressSanitizer and
+# UndefinedBehaviorSanitizer (gcc's runtimes, which the process must preload;
+# tests/run_sanitizers.py does that).
+_SANITIZE = os.environ.get("EVO_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "libevo_oracle_san.so" if _SANITIZE else "libevo_oracle.so")
 _lib = None
 
 
@@ -36,8 +40,10 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
+    san = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"] \
+        if _SANITIZE else []
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", *san, "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB

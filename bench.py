@@ -36,6 +36,11 @@ UNIT = "TFLOP/s"
 PEAK_BF16_MFMA_TFLOPS = 2500.0   # dense bf16 matrix
 PEAK_FP32_VECTOR_TFLOPS = 157.3  # fp32 vector ALU
 PEAK_HBM_GBS = 8000.0
+# Vector ALU issue peak for the non-packed 32-bit operations these kernels use:
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane operations per second (the
+# 157.3 TFLOP/s figure counts an FMA as two flops and two lanes per packed
+# instruction; packed fp32 instructions are not used here).
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 # Algorithmic work per launch of each kernel, in multiples of R*N^2*H*d flops
 # (score elements times head_dim), with the unit that bounds it.
@@ -50,6 +55,18 @@ KERNEL_FLOP_FACTOR = {
     "bwd_dq_vector": (6.0, "alu"),
     "bwd_dkdv_vector": (8.0, "alu"),
     "bwd_dbias_vector": (4.0, "alu"),
+}
+
+# Vector-ALU work each bf16 kernel needs per score element, in 32-bit lane
+# operations: the scale (or the FMA that also subtracts the reference point), the
+# exp2, the running sum (forward) or dS = P dP (backward) or the dBias
+# accumulation, and the packing of P and dS to bf16 (one cvt_pk per two values).
+KERNEL_VALU_OPS = {
+    "fwd_mfma": 3.5,        # fma, exp2, add, cvt/2
+    "bwd_fused_mfma": 4.0,  # mul, exp2, mul, cvt/2 for P and for dS
+    "bwd_dkdv_mfma": 4.0,
+    "bwd_dq_mfma": 3.5,     # mul, exp2, mul, cvt/2 for dS
+    "bwd_dbias_mfma": 3.0,  # mul, exp2, fma
 }
 
 
@@ -749,9 +766,11 @@ def main():
     flops_step = w.flops_fwd_bwd() * len(variants)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    # Roofline of the dominant kernel.
+    # Roofline of the dominant kernel: its matrix-core figure and, for the bf16
+    # kernels, its vector-ALU figure; "roofline" is the nearer of the two roofs
+    # (the larger fraction) and "roofline_other" the farther.
     dom = max(kernels.items(), key=lambda kv: kv[1][1]) if kernels else None
-    roofline = None
+    roofline = roofline_other = None
     if dom:
         name, (count, tot) = dom
         avg_ms = tot / count
@@ -764,6 +783,17 @@ def main():
             roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                         "frac": achieved / peak, "traffic": recorded_traffic(name, w.name), "kernel": name,
                         "avg_launch_ms": avg_ms, "launches": count}
+        if name in KERNEL_VALU_OPS and roofline is not None:
+            scores = units / w.head_dim
+            ach = KERNEL_VALU_OPS[name] * scores / (avg_ms * 1e-3) / 1e12
+            valu = {"bound": "alu", "achieved": ach, "peak": PEAK_VALU_TOPS, "unit": "T lane-ops/s",
+                    "frac": ach / PEAK_VALU_TOPS, "traffic": roofline["traffic"], "kernel": name,
+                    "avg_launch_ms": avg_ms, "launches": count,
+                    "ops_per_score": KERNEL_VALU_OPS[name]}
+            if valu["frac"] > roofline["frac"]:
+                roofline, roofline_other = valu, roofline
+            else:
+                roofline_other = valu
 
     calibration = copy_calibration(dev) if args.copy_calibration else None
 
@@ -782,6 +812,7 @@ def main():
                      "frac_of_bf16_peak": w.flops_fwd() * len(variants) / (fwd_ms * 1e-3) / 1e12
                      / PEAK_BF16_MFMA_TFLOPS},
         "roofline": roofline,
+        "roofline_other": roofline_other,
         "cpu_baseline": cpu,
         "kernels_ms_per_step": {k: tot / args.steps for k, (c, tot) in kernels.items()},
         "events_pass_ms_per_step": None if args.no_kernel_timing else events_ms_per_step,

@@ -43,8 +43,9 @@
  * ---------------------------------------------------------------- ownership
  * Every pointer argument except `stream` is a device pointer owned by the
  * caller.  The library allocates no device memory and keeps no state between
- * calls beyond a thread-local error string and, while timing is enabled, the
- * per-kernel timing record (see below).  Outputs are overwritten, never
+ * calls beyond a thread-local error string, the device address of
+ * evoattn_fwd_noalloc's static scratch (one per device, looked up once) and,
+ * while timing is enabled, the per-kernel timing record (see below).  Outputs are overwritten, never
  * accumulated.  Scratch space is passed in as `workspace` of at least the size
  * the matching *_workspace_bytes query returns; its contents on entry do not
  * matter and on return are unspecified.  Inputs and outputs must not overlap.
@@ -87,30 +88,40 @@ typedef enum {
   EVOATTN_BF16 = 1
 } evoattn_dtype_t;
 
-/* Returns EVOATTN_ABI_VERSION of the built library. */
+/* Returns EVOATTN_ABI_VERSION of the built library.  (Interface versioning of
+ * this boundary; not part of the pages' method.) */
 int evoattn_abi_version(void);
 
-/* Static, never-NULL name of a status code. */
+/* Static, never-NULL name of a status code.  (Error reporting of this boundary;
+ * not part of the pages' method.) */
 const char* evoattn_status_string(int status);
 
-/* Description of the last failed call on the calling thread ("" if none). */
+/* Description of the last failed call on the calling thread ("" if none).
+ * (Error reporting of this boundary; not part of the pages' method.) */
 const char* evoattn_last_error_detail(void);
 
-/* Bytes of workspace evoattn_fwd needs for this problem (may be 0): for bf16
+/* Scratch of the tile-by-tile forward (gist.science MegaFold technical summary,
+ * Methodik section 1: the logits stay on chip, so the scratch is O(R*N + H*N*N)).
+ * Bytes of workspace evoattn_fwd needs for this problem (may be 0): for bf16
  * the sqrt(d)-scaled bias as fp32 tiles (O(H*N*N)) and, for head_dim <= 32, the
  * key-side mask operands and each row's last unmasked key (O(R*N)).
  * Returns 0 and records an error detail if the problem is invalid. */
 size_t evoattn_fwd_workspace_bytes(int64_t rows, int64_t n, int64_t heads,
                                    int64_t head_dim, int dtype);
 
-/* Bytes of workspace evoattn_bwd needs for this problem (row statistics and
- * the fixed-order dBias partial sums; O(R*H*N + H*N*N)). */
+/* Scratch of the recomputing backward (same passage: the memory-efficient kernel
+ * runs in the backward too).  Bytes of workspace evoattn_bwd needs for this
+ * problem (row statistics, the tiled bias and the fixed-order dBias partial sums;
+ * O(R*H*N + H*N*N)). */
 size_t evoattn_bwd_workspace_bytes(int64_t rows, int64_t n, int64_t heads,
                                    int64_t head_dim, int dtype);
 
-/* Forward.  Inputs q, k, v (dtype, layout above), bias [H,N,N] (dtype; NULL
- * means zero), mask [R,N] fp32 (NULL means zero).  Outputs o (dtype, same
- * layout as q) and lse [R,H,N] fp32 (NULL if no backward will follow). */
+/* Forward of EvoAttention (gist.science MegaFold technical summary, Methodik
+ * section 1 "EvoFlash-3D": the logits of each row are formed tile by tile on
+ * chip and normalised with an online softmax; the pair bias is added to every
+ * row).  Inputs q, k, v (dtype, layout above), bias [H,N,N] (dtype; NULL means
+ * zero), mask [R,N] fp32 (NULL means zero).  Outputs o (dtype, same layout as
+ * q) and lse [R,H,N] fp32 (NULL if no backward will follow). */
 evoattn_status_t evoattn_fwd(int64_t rows, int64_t n, int64_t heads, int64_t head_dim,
                              int dtype, int transpose,
                              const void* q, const void* k, const void* v,
@@ -135,10 +146,12 @@ evoattn_status_t evoattn_fwd_noalloc(int64_t rows, int64_t n, int64_t heads, int
                                      const void* bias, const float* mask,
                                      void* o, float* lse, void* stream);
 
-/* Backward of sum(o * dout).  Inputs: the forward's inputs, its outputs o and
- * lse (required), and dout (dtype, layout of o).  Outputs dq, dk, dv (dtype,
- * layout of q) and dbias [H,N,N] fp32 (NULL to skip).  The mask receives no
- * gradient. */
+/* Backward of EvoAttention (same passage: the memory-efficient kernel also runs
+ * in the backward pass, recomputing the probabilities from lse on chip; dbias is
+ * the sum over rows of the bias gradient, reduced in a fixed order).  Backward
+ * of sum(o * dout).  Inputs: the forward's inputs, its outputs o and lse
+ * (required), and dout (dtype, layout of o).  Outputs dq, dk, dv (dtype, layout
+ * of q) and dbias [H,N,N] fp32 (NULL to skip).  The mask receives no gradient. */
 evoattn_status_t evoattn_bwd(int64_t rows, int64_t n, int64_t heads, int64_t head_dim,
                              int dtype, int transpose,
                              const void* q, const void* k, const void* v,
@@ -148,7 +161,8 @@ evoattn_status_t evoattn_bwd(int64_t rows, int64_t n, int64_t heads, int64_t hea
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- timing
- * Per-kernel timing, a profiling aid.  While enabled, every kernel this
+ * Per-kernel timing, a profiling aid (the measurement of the path, not part of
+ * the pages' method).  While enabled, every kernel this
  * library launches is bracketed by two HIP events recorded on the stream it is
  * launched on, so the measured span is that kernel's time on its stream.
  * Disabled by default; enabling costs two event records per launch.

@@ -127,11 +127,17 @@ def test_fwd_unsupported_shapes_fail_loudly():
 # ================================================================ backward
 #
 # Every matrix-core operand of the backward (y, xhat, dout, da, db, h) is bf16,
-# i.e. rounded by at most 2^-8 of itself, and each result sums n*C or T such
-# terms in fp32.  Independent roundings give each gradient a relative error of
-# a few tenths of a percent of its max norm (the forward's is 0.3-0.5 %); dx also
-# carries its own final rounding.  The test requires max|err| <= 2e-2 max|ref|
-# for dx and every weight gradient, and bit-identical results from two calls.
+# i.e. rounded by at most 2^-9 of itself (round to nearest, 8 significant bits),
+# and each result sums n*C or T such terms in fp32.  The backward rounds x-hat
+# twice where the forward rounds it once: the dx kernel forms y from the
+# bf16-rounded x-hat it hands to the weight-gradient kernel (y = gamma bf16(xhat)
+# + beta, rounded again), so y, a and b carry two roundings, at most about 2^-8
+# relative together, while the layer-norm part of dx uses the fp32 x-hat.
+# Independent roundings of that size give each gradient a relative error of a few
+# tenths of a percent of its max norm (the forward's is 0.3-0.5 %, the measured
+# backward errors 0.3-0.5 %); dx also carries its own final rounding.  The test
+# requires max|err| <= 2e-2 max|ref| for dx and every weight gradient, and
+# bit-identical results from two calls.
 
 BWD_REL = 2e-2
 

@@ -264,25 +264,42 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
 
   // Block b: everything issued one block earlier has arrived and every wave has
   // finished block b - 1 (its stage and its dS tiles are complete; the buffers of
-  // block b - 2 are free).  Block b + 1's copies and bias start at once.
-  auto step = [&](int b, auto s_c) __attribute__((always_inline)) {
+  // block b - 2 are free).  Block b + 1's copies and bias start at once.  The two
+  // roles run separate copies of the loop (the same number of barriers), so that
+  // neither role's registers have to be reconciled with the other's.
+  auto step = [&](int b, auto s_c, auto pair_c) __attribute__((always_inline)) {
     constexpr int s = decltype(s_c)::value;
+    constexpr bool PAIR = decltype(pair_c)::value;
     wait_vmcnt<0>();
     barrier();
     retire(ta.bias[s]);
-    if (pair_wave) retire(tb.bias[s]);
+    if constexpr (PAIR) retire(tb.bias[s]);
     if (b + 1 < nkt) {
       issue_block(b + 1, stage0 + (s ^ 1) * STAGE);
       load_bias(ta, ta.bias[s ^ 1], b + 1);
-      if (pair_wave) load_bias(tb, tb.bias[s ^ 1], b + 1);
+      if constexpr (PAIR) load_bias(tb, tb.bias[s ^ 1], b + 1);
     }
     const uint32_t st = stage0 + s * STAGE, dsb = ds0 + s * (kFTiles * kDsBytes);
-    if (pair_wave) {
+    if constexpr (PAIR) {
       tile_row(b, st, ta, ta.bias[s], dsb);
       tile_row(b, st, tb, tb.bias[s], dsb);
     } else {
       if (dq_wave && b >= 1) dq_tile(b - 1, ds0 + (s ^ 1) * (kFTiles * kDsBytes));
       tile_row(b, st, ta, ta.bias[s], dsb);
+    }
+  };
+  auto run = [&](auto pair_c) __attribute__((always_inline)) {
+    constexpr bool PAIR = decltype(pair_c)::value;
+    load_bias(ta, ta.bias[0], 0);
+    if constexpr (PAIR) load_bias(tb, tb.bias[0], 0);
+    for (int b = 0; b < nkt; b += 2) {
+      step(b, std::integral_constant<int, 0>(), pair_c);
+      if (b + 1 < nkt) step(b + 1, std::integral_constant<int, 1>(), pair_c);
+    }
+    wait_vmcnt<0>();
+    barrier();
+    if constexpr (!PAIR) {
+      if (dq_wave) dq_tile(nkt - 1, ds0 + ((nkt - 1) & 1) * (kFTiles * kDsBytes));
     }
   };
 
@@ -295,15 +312,10 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
     stk.issue(k_res, kvbase, 0, p.N, wave, dummy);
   }
   issue_block(0, stage0);
-  load_bias(ta, ta.bias[0], 0);
-  if (pair_wave) load_bias(tb, tb.bias[0], 0);
-  for (int b = 0; b < nkt; b += 2) {
-    step(b, std::integral_constant<int, 0>());
-    if (b + 1 < nkt) step(b + 1, std::integral_constant<int, 1>());
-  }
-  wait_vmcnt<0>();
-  barrier();
-  if (dq_wave) dq_tile(nkt - 1, ds0 + ((nkt - 1) & 1) * (kFTiles * kDsBytes));
+  if (pair_wave)
+    run(std::true_type());
+  else
+    run(std::false_type());
 
   auto store_tile = [&](const KeyTile& t) __attribute__((always_inline)) {
     const int key = t.kt * 32 + (lane & 31);

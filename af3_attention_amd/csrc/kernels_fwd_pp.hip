@@ -500,6 +500,8 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
   finalize(I1(), cur);
 }
 
+}  // namespace
+
 // Compute units of the current device (cached per device).
 int device_cus() {
   static int cus[64] = {0};
@@ -512,6 +514,8 @@ int device_cus() {
   }
   return cus[dev];
 }
+
+namespace {
 
 template <int D>
 hipError_t fwd_pp_dispatch(const Problem& p, const FwdArgs& a, float* bias_t, u32x4* kaug, int* last_live,

@@ -77,6 +77,24 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(Problem p, BwdArgs a)
   const Split3 nd = split3(-s);
   reinterpret_cast<u32x4*>(a.qaug)[rhj] =
       u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), nd.hi | (nd.mid << 16), nd.lo};
+  if (a.qops) {
+    // The fused backward's per-query operands, complete: the S step's query side
+    // [-a, -a, -a, 1, 1, 1, 0, 0] and the dP step's [-D, -D, -D, 0, ...]; the
+    // padding queries N .. Np - 1 of the row get the dead-query side (every
+    // probability 0) from the thread of query N - 1.
+    // Layout per (r, h): blocks of 32 queries, each the 32 S-step operands then
+    // the 32 dP-step operands (so that a block is 1 KB of consecutive entries).
+    const int np = (p.N + 31) / 32 * 32;
+    u32x4* qo = reinterpret_cast<u32x4*>(a.qops) + 2 * (static_cast<int64_t>(r) * p.H + h) * np;
+    auto put = [&](int jj, u32x4 sq, u32x4 dq) {
+      qo[(jj >> 5) * 64 + (jj & 31)] = sq;
+      qo[(jj >> 5) * 64 + 32 + (jj & 31)] = dq;
+    };
+    put(j, u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), kBf16One | (kBf16One << 16), 0u},
+        u32x4{nd.hi | (nd.mid << 16), nd.lo, 0u, 0u});
+    if (j == p.N - 1)
+      for (int jj = p.N; jj < np; ++jj) put(jj, dead_query_aug(), u32x4{0u, 0u, 0u, 0u});
+  }
   if (h == 0) {
     const float m = a.mask ? a.mask[static_cast<int64_t>(r) * p.N + j] : 0.f;
     const Split3 sm = split3(fmaxf(sd * m, -kHuge));
@@ -125,7 +143,7 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_q, 
 size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdLayout {
-  size_t qaug, kaug, bias, part, total;
+  size_t qaug, kaug, bias, part, qops, total;
 };
 BwdLayout bwd_layout(const Problem& p) {
   BwdLayout l;
@@ -134,14 +152,16 @@ BwdLayout bwd_layout(const Problem& p) {
   l.kaug = align_up(static_cast<size_t>(p.R) * p.N * 16);
   l.bias = align_up(tiled_bias_bytes(p));
   l.part = groups > 1 ? align_up(static_cast<size_t>(groups) * p.H * p.N * p.N * sizeof(float)) : 0;
-  l.total = l.qaug + l.kaug + 2 * l.bias + l.part;
+  l.qops = bwd_fused_supported(p) ? align_up(static_cast<size_t>(p.R) * p.H * ((p.N + 31) / 32 * 32) * 32) : 0;
+  l.total = l.qaug + l.kaug + 2 * l.bias + l.part + l.qops;
   return l;
 }
 
 }  // namespace
 
 // Workspace: qaug [R,H,N] x 16 B | kaug [R,N] x 16 B |
-// tiled bias, query lanes | tiled bias, key lanes | dbias partials [G,H,N,N] fp32.
+// tiled bias, query lanes | tiled bias, key lanes | dbias partials [G,H,N,N] fp32 |
+// fused-backward query operands [R,H,Np] x 32 B (when that kernel runs).
 size_t bwd_mfma_workspace_bytes(const Problem& p) { return bwd_layout(p).total; }
 
 hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& args, void* ws, hipStream_t s) {
@@ -159,6 +179,8 @@ hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& args, void* ws, hipS
   float* bias_k = reinterpret_cast<float*>(base);
   base += l.bias;
   float* part = reinterpret_cast<float*>(base);
+  base += l.part;
+  a.qops = l.qops ? base : nullptr;
   switch (p.D) {
     case 8: return bwd_mfma_dispatch<8>(p, a, bias_q, bias_k, part, groups, s);
     case 16: return bwd_mfma_dispatch<16>(p, a, bias_q, bias_k, part, groups, s);

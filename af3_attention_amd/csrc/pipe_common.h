@@ -332,6 +332,8 @@ hipError_t launch_fwd_prep(const Problem& p, const void* bias, const float* mask
                            int* last_live, hipStream_t s);
 // dQ, dK, dV in one pass (kernels_bwd_fused.hip), for head_dim <= 32 and N <= 384;
 // needs the per-row split operands (qaug, kaug) and the key-lane bias tiles.
+// Compute units of the current device (cached per device).
+int device_cus();
 bool bwd_fused_supported(const Problem& p);
 hipError_t launch_bwd_fused(const Problem& p, const BwdArgs& a, const float* bias_k, hipStream_t s);
 // bf16 forward for head_dim 8, 16, 32 (kernels_fwd_pp.hip).

@@ -43,9 +43,10 @@ struct BwdArgs {
   float* dbias;       // [H,N,N] or nullptr
   float* delta;       // workspace [R,H,N]: sum_c dout*o per softmax row
   void* qaug;         // MFMA path workspace [R,H,N] x 16 B: per-query split operands (lse, delta)
+                      // for the dq and dkdv kernels, nullptr when they do not run
   void* kaug;         // MFMA path workspace [R,N] x 16 B: per-key split operands (mask)
-  void* qops;         // fused backward workspace [R,H,Np] x 32 B (Np = N rounded up to 32):
-                      // per query the complete MFMA operands of the S and dP steps, nullptr otherwise
+  void* qops;         // MFMA path workspace [R,H,Np] x 32 B (Np = N rounded up to 128): per
+                      // query the complete operands of the S and dP steps (fused, dbias)
   float* scratch;     // further workspace (path specific)
   size_t scratch_bytes;
 };

@@ -31,8 +31,8 @@ using namespace pipe;
 
 constexpr int kDbT = 128;      // tile edge (queries and keys)
 constexpr int kDbThreads = 512;  // 8 waves: 4 key tiles x 2 query halves
-// LDS ring of rows (copies run db_stages - 1 rows ahead): four stages of 34.5 KB
-// up to d = 32, two of 66 KB at d = 64.
+// LDS ring of rows (copies run db_stages - 1 rows ahead): four stages of 38 KB
+// up to d = 32, two of 70 KB at d = 64.
 template <int D>
 constexpr int db_stages() { return D >= 64 ? 2 : 4; }
 
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
                                                                    const float* __restrict__ bias_k, int nt,
                                                                    int groups, float* __restrict__ out) {
   constexpr int TB = Tile<D, kDbT>::BYTES;
-  constexpr int STATS = 2 * kDbT * 16;  // query-side (lse, D) and key-side (mask) split operands
+  constexpr int STATS = 3 * kDbT * 16;  // query-side (lse, D; 32 B per query) and key-side (mask) operands
   constexpr int STAGE = 4 * TB + STATS;
   constexpr int NS = db_stages<D>();
   constexpr int DUMMY = NS * STAGE;  // 1 KB target of dummy copies
@@ -91,7 +91,8 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
   const uint16_t* const vp = static_cast<const uint16_t*>(a.v);
 
   // Copies of row r into stage s: Q, dO (queries q0..), K, V (keys k0..), and one
-  // 64-entry piece of the split operands for each of waves 0..3.
+  // 64-entry piece of the split operands for each of waves 0..5: the 128 queries'
+  // pre-formed operands (4 KB, waves 0..3) and the 128 keys' (2 KB, waves 4, 5).
   auto issue_row = [&](int r, auto stage_c) {
     constexpr int s = decltype(stage_c)::value;
     const uint32_t st = lds0 + s * STAGE;
@@ -102,15 +103,16 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
                          uniform_ptr(reinterpret_cast<const char*>(vp + rh))};
     stager.issue(st, qd, q0, p.N, wave, lds0 + DUMMY);
     stager.issue(st + 2 * TB, kv, k0, p.N, wave, lds0 + DUMMY);
-    const int64_t rhn = (static_cast<int64_t>(r) * p.H + h) * p.N;
-    const int piece = wave & 1;
-    if (wave < 2) {
-      copy_rows16(static_cast<const u32x4*>(a.qaug) + rhn, q0 + 64 * piece, p.N, st + 4 * TB + 1024 * piece, lane);
-    } else if (wave < 4) {
+    if (wave < 4) {
+      const u32x4* qo = static_cast<const u32x4*>(a.qops) +
+                        2 * (static_cast<int64_t>(r) * p.H + h) * qops_queries(p.N) + 2 * q0 + 64 * wave;
+      copy16_to_lds(uniform_ptr(qo), static_cast<uint32_t>(lane) * 16, st + 4 * TB + 1024 * wave);
+    } else if (wave < 6) {
+      const int piece = wave & 1;
       copy_rows16(static_cast<const u32x4*>(a.kaug) + static_cast<int64_t>(r) * p.N, k0 + 64 * piece, p.N,
-                  st + 4 * TB + kDbT * 16 + 1024 * piece, lane);
+                  st + 4 * TB + 2 * kDbT * 16 + 1024 * piece, lane);
     } else {  // keep one operand copy per wave and row, so that waits can count them
-      copy16_to_lds(uniform_ptr(a.qaug), 0u, lds0 + DUMMY);
+      copy16_to_lds(uniform_ptr(a.kaug), 0u, lds0 + DUMMY);
     }
   };
 
@@ -137,16 +139,15 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
       kop[ks] = rd.rows_operand(tk, wk * 32, ks, lane);
       vop[ks] = rd.rows_operand(tv, wk * 32, ks, lane);
     }
-    u32x4 s_key = lds_load16(stats + kDbT * 16 + kl * 16);
+    u32x4 s_key = lds_load16(stats + 2 * kDbT * 16 + kl * 16);
     if (lane >> 5) s_key = u32x4{0u, 0u, 0u, 0u};
 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int x0 = (2 * wq + t) * 32;      // first query of this tile within the block
       const int jl = x0 + (lane & 31);       // this lane's query (as an A-operand row)
-      const u32x4 qa = lds_load16(stats + jl * 16);
-      const u32x4 s_q = q0 + jl < p.N ? u32x4{qa[0], qa[1], kBf16One | (kBf16One << 16), 0u} : dead_query_aug();
-      const u32x4 dp_q = {qa[2], qa[3], 0u, 0u};
+      const u32x4 s_q = lds_load16(stats + (jl >> 5) * 1024 + (jl & 31) * 16);
+      const u32x4 dp_q = lds_load16(stats + (jl >> 5) * 1024 + 512 + (jl & 31) * 16);
       f32x16 sacc = mma(rd.rows_operand(tq, x0, 0, lane), kop[0], bias[t]);
 #pragma unroll
       for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tq, x0, ks, lane), kop[ks], sacc);

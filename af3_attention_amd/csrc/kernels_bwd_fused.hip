@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
 
   const int wave = wave_id(), lane = threadIdx.x & 63, half = lane >> 5;
   const int nkt = (p.N + 31) / 32;  // key tiles = query blocks
-  const int np = nkt * 32;
+  const int np = qops_queries(p.N);
   const bool pair_wave = wave < 4;  // two key tiles; otherwise one tile and dQ
   const float sd = sqrtf(static_cast<float>(D));
   const float c1 = kLog2e / sd;

@@ -43,9 +43,11 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restri
 }
 
 // Per-row terms of the backward, one thread per (r, j, h) in memory order (so a
-// wave reads contiguous 2*d-byte pieces of O and dO):
-//   qaug[r,h,j]  = the query-side split operands of -sqrt(d) lse and of -D,
-//                  D = sum_c dout[r,j,h,c] o[r,j,h,c]
+// wave reads contiguous 2*d-byte pieces of O and dO), D = sum_c dout[r,j,h,c] o[r,j,h,c]:
+//   qops[r,h,j]  = the complete query-side operands of the S and dP steps
+//                  (-sqrt(d) lse and -D, split; dbias and the fused kernel)
+//   qaug[r,h,j]  = the same in the packed form of the dq and dkdv kernels (only
+//                  when those run)
 //   kaug[r,j]    = the key-side split operands of sqrt(d) mask (threads with h = 0)
 // (layouts of the operands: pipe_common.h).
 template <int D>
@@ -75,26 +77,22 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(Problem p, BwdArgs a)
   const float sd = sqrtf(static_cast<float>(D));
   const Split3 na = split3(-lse_term(a.lse[rhj], sd, true));
   const Split3 nd = split3(-s);
-  reinterpret_cast<u32x4*>(a.qaug)[rhj] =
-      u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), nd.hi | (nd.mid << 16), nd.lo};
-  if (a.qops) {
-    // The fused backward's per-query operands, complete: the S step's query side
-    // [-a, -a, -a, 1, 1, 1, 0, 0] and the dP step's [-D, -D, -D, 0, ...]; the
-    // padding queries N .. Np - 1 of the row get the dead-query side (every
-    // probability 0) from the thread of query N - 1.
-    // Layout per (r, h): blocks of 32 queries, each the 32 S-step operands then
-    // the 32 dP-step operands (so that a block is 1 KB of consecutive entries).
-    const int np = (p.N + 31) / 32 * 32;
-    u32x4* qo = reinterpret_cast<u32x4*>(a.qops) + 2 * (static_cast<int64_t>(r) * p.H + h) * np;
-    auto put = [&](int jj, u32x4 sq, u32x4 dq) {
-      qo[(jj >> 5) * 64 + (jj & 31)] = sq;
-      qo[(jj >> 5) * 64 + 32 + (jj & 31)] = dq;
-    };
-    put(j, u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), kBf16One | (kBf16One << 16), 0u},
-        u32x4{nd.hi | (nd.mid << 16), nd.lo, 0u, 0u});
-    if (j == p.N - 1)
-      for (int jj = p.N; jj < np; ++jj) put(jj, dead_query_aug(), u32x4{0u, 0u, 0u, 0u});
-  }
+  if (a.qaug)
+    reinterpret_cast<u32x4*>(a.qaug)[rhj] =
+        u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), nd.hi | (nd.mid << 16), nd.lo};
+  // The per-query operands complete (layout: qops_queries): the S step's query
+  // side and the dP step's; the padding queries N .. Np - 1 of the row get the
+  // dead-query side (every probability 0) from the thread of query N - 1.
+  const int np = qops_queries(p.N);
+  u32x4* qo = reinterpret_cast<u32x4*>(a.qops) + 2 * (static_cast<int64_t>(r) * p.H + h) * np;
+  auto put = [&](int jj, u32x4 sq, u32x4 dq) {
+    qo[(jj >> 5) * 64 + (jj & 31)] = sq;
+    qo[(jj >> 5) * 64 + 32 + (jj & 31)] = dq;
+  };
+  put(j, u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), kBf16One | (kBf16One << 16), 0u},
+      u32x4{nd.hi | (nd.mid << 16), nd.lo, 0u, 0u});
+  if (j == p.N - 1)
+    for (int jj = p.N; jj < np; ++jj) put(jj, dead_query_aug(), u32x4{0u, 0u, 0u, 0u});
   if (h == 0) {
     const float m = a.mask ? a.mask[static_cast<int64_t>(r) * p.N + j] : 0.f;
     const Split3 sm = split3(fmaxf(sd * m, -kHuge));
@@ -148,20 +146,20 @@ struct BwdLayout {
 BwdLayout bwd_layout(const Problem& p) {
   BwdLayout l;
   const int groups = dbias_pipe_groups(p);
-  l.qaug = align_up(static_cast<size_t>(p.R) * p.H * p.N * 16);
+  l.qaug = bwd_fused_supported(p) ? 0 : align_up(static_cast<size_t>(p.R) * p.H * p.N * 16);
   l.kaug = align_up(static_cast<size_t>(p.R) * p.N * 16);
   l.bias = align_up(tiled_bias_bytes(p));
   l.part = groups > 1 ? align_up(static_cast<size_t>(groups) * p.H * p.N * p.N * sizeof(float)) : 0;
-  l.qops = bwd_fused_supported(p) ? align_up(static_cast<size_t>(p.R) * p.H * ((p.N + 31) / 32 * 32) * 32) : 0;
+  l.qops = align_up(static_cast<size_t>(p.R) * p.H * qops_queries(p.N) * 32);
   l.total = l.qaug + l.kaug + 2 * l.bias + l.part + l.qops;
   return l;
 }
 
 }  // namespace
 
-// Workspace: qaug [R,H,N] x 16 B | kaug [R,N] x 16 B |
+// Workspace: qaug [R,H,N] x 16 B (when the dq and dkdv kernels run) | kaug [R,N] x 16 B |
 // tiled bias, query lanes | tiled bias, key lanes | dbias partials [G,H,N,N] fp32 |
-// fused-backward query operands [R,H,Np] x 32 B (when that kernel runs).
+// query operands qops [R,H,Np] x 32 B (Np = qops_queries(N)).
 size_t bwd_mfma_workspace_bytes(const Problem& p) { return bwd_layout(p).total; }
 
 hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& args, void* ws, hipStream_t s) {
@@ -169,8 +167,8 @@ hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& args, void* ws, hipS
   const int groups = dbias_pipe_groups(p);
   char* base = static_cast<char*>(ws);
   BwdArgs a = args;
-  a.delta = nullptr;  // D lives in qaug on this path
-  a.qaug = base;
+  a.delta = nullptr;  // D lives in qops (and qaug) on this path
+  a.qaug = l.qaug ? base : nullptr;
   base += l.qaug;
   a.kaug = base;
   base += l.kaug;
@@ -180,7 +178,7 @@ hipError_t launch_bwd_mfma(const Problem& p, const BwdArgs& args, void* ws, hipS
   base += l.bias;
   float* part = reinterpret_cast<float*>(base);
   base += l.part;
-  a.qops = l.qops ? base : nullptr;
+  a.qops = base;
   switch (p.D) {
     case 8: return bwd_mfma_dispatch<8>(p, a, bias_q, bias_k, part, groups, s);
     case 16: return bwd_mfma_dispatch<16>(p, a, bias_q, bias_k, part, groups, s);

@@ -332,6 +332,13 @@ hipError_t launch_fwd_prep(const Problem& p, const void* bias, const float* mask
                            int* last_live, hipStream_t s);
 // dQ, dK, dV in one pass (kernels_bwd_fused.hip), for head_dim <= 32 and N <= 384;
 // needs the per-row split operands (qaug, kaug) and the key-lane bias tiles.
+// Queries per attention row in the backward's pre-formed query operands (qops):
+// N rounded up to 128, so that every 32-query block of a 128-query tile exists.
+// Layout per (r, h): blocks of 32 queries, each 32 S-step operands
+// [-a, -a, -a, 1, 1, 1, 0, 0] (a = sqrt(d) lse, split) then 32 dP-step operands
+// [-D, -D, -D, 0, ...]; padding queries hold the dead-query S operand.
+__host__ __device__ inline int qops_queries(int n) { return (n + 127) / 128 * 128; }
+
 // Compute units of the current device (cached per device).
 int device_cus();
 bool bwd_fused_supported(const Problem& p);

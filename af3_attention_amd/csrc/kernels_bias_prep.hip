@@ -8,52 +8,12 @@
 namespace evo {
 namespace {
 
-// One 32 x 32 bias tile (query tile qt, key tile kt) of head h.
-template <typename T>
-__device__ __forceinline__ void bias_tile(const Problem& p, const T* __restrict__ bias, float* __restrict__ out_q,
-                                          float* __restrict__ out_k, int nt, int tile) {
-  __shared__ float tile_lds[32][33];  // [query][key], padded
-  const int kt = tile % nt;
-  const int qt = (tile / nt) % nt;
-  const int h = tile / (nt * nt);
-  const float sd = sqrtf(static_cast<float>(p.D));
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int jj = (t >> 5) + 8 * i, kk = t & 31;
-    const int j = qt * 32 + jj, k = kt * 32 + kk;
-    float val;
-    if (k >= p.N) {
-      val = -INFINITY;
-    } else if (j >= p.N || bias == nullptr) {
-      val = 0.f;
-    } else {
-      val = sd * Elem<T>::load(bias, (static_cast<int64_t>(h) * p.N + j) * p.N + k);
-    }
-    tile_lds[jj][kk] = val;
-  }
-  __syncthreads();
-  // Thread t writes floats 4t..4t+3 of the tile: register group g = t / 64 of lane
-  // l = t % 64, accumulator rows 8g + 4(l / 32) + e, column l % 32.
-  const int g = t >> 6, lane = t & 63;
-  const int row0 = 8 * g + 4 * (lane >> 5), col = lane & 31;
-  const int64_t off = (((static_cast<int64_t>(h) * nt + qt) * nt + kt) * 1024) + 4 * t;
-  if (out_q)  // query lanes: rows are keys, the column is the query
-    *reinterpret_cast<float4*>(out_q + off) =
-        make_float4(tile_lds[col][row0], tile_lds[col][row0 + 1], tile_lds[col][row0 + 2], tile_lds[col][row0 + 3]);
-  if (out_k)  // key lanes: rows are queries, the column is the key
-    *reinterpret_cast<float4*>(out_k + off) =
-        make_float4(tile_lds[row0][col], tile_lds[row0 + 1][col], tile_lds[row0 + 2][col], tile_lds[row0 + 3][col]);
-}
-
 // Tiled layout (see pipe_common.h).  One workgroup per 32 x 32 block (query tile
-// qt, key tile kt) of one head: the block is read once (coalesced rows of 32 keys)
-// into LDS, then written in the query-lane order to out_q and in the key-lane
-// order to out_k (each skipped when NULL), each as 256 coalesced 16-byte stores.
+// qt, key tile kt) of one head.
 template <typename T>
 __global__ __launch_bounds__(256) void bias_tiles_kernel(Problem p, const T* __restrict__ bias, float* __restrict__ out_q,
                                                          float* __restrict__ out_k, int nt) {
-  bias_tile(p, bias, out_q, out_k, nt, blockIdx.x);
+  pipe::bias_tile(p, bias, out_q, out_k, nt, blockIdx.x);
 }
 
 // Forward pre-pass: the bias tiles in the query-lane order (blocks 0 .. tiles - 1)
@@ -66,7 +26,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Problem p, const T* __res
                                                        float* __restrict__ out_q, uint4* __restrict__ kaug,
                                                        int* __restrict__ last_live, int nt, int tiles) {
   if (static_cast<int>(blockIdx.x) < tiles) {
-    bias_tile(p, bias, out_q, static_cast<float*>(nullptr), nt, blockIdx.x);
+    pipe::bias_tile(p, bias, out_q, static_cast<float*>(nullptr), nt, blockIdx.x);
     return;
   }
   __shared__ int red[4];

@@ -50,10 +50,18 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restri
 //                  when those run)
 //   kaug[r,j]    = the key-side split operands of sqrt(d) mask (threads with h = 0)
 // (layouts of the operands: pipe_common.h).
+// The same launch also forms the sqrt(d) * bias tiles the later kernels read:
+// blocks 0 .. tiles - 1 each form one tile (pipe::bias_tile), so that this small
+// pass overlaps the row terms instead of taking a launch of its own.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_rowterms_kernel(Problem p, BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_rowterms_kernel(Problem p, BwdArgs a, float* __restrict__ bias_q,
+                                                           float* __restrict__ bias_k, int nt, int tiles) {
   using namespace pipe;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (static_cast<int>(blockIdx.x) < tiles) {
+    bias_tile(p, static_cast<const uint16_t*>(a.bias), bias_q, bias_k, nt, blockIdx.x);
+    return;
+  }
+  const int64_t idx = static_cast<int64_t>(blockIdx.x - tiles) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(p.R) * p.H * p.N;
   if (idx >= total) return;
   const int h = static_cast<int>(idx % p.H);
@@ -109,18 +117,21 @@ template <int D>
 hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_q, float* bias_k, float* dbias_part,
                              int groups, hipStream_t s) {
   hipError_t e;
+  const bool fused = bwd_fused_supported(p);
   {
+    // Row terms and the bias tiles: key-lane tiles always, query-lane tiles for
+    // the dq kernel.
     const int64_t rows_total = static_cast<int64_t>(p.R) * p.H * p.N;
-    KernelTimer timer("bwd_rowterms", s);
-    hipLaunchKernelGGL((bwd_rowterms_kernel<D>), dim3(static_cast<unsigned>((rows_total + 255) / 256)), dim3(256), 0,
-                       s, p, a);
+    const int nt = bias_tiles(p.N);
+    const int tiles = p.H * nt * nt;
+    KernelTimer timer("bwd_prep", s);
+    hipLaunchKernelGGL((bwd_rowterms_kernel<D>), dim3(static_cast<unsigned>(tiles + (rows_total + 255) / 256)),
+                       dim3(256), 0, s, p, a, fused ? nullptr : bias_q, bias_k, nt, tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (bwd_fused_supported(p)) {
-    if ((e = launch_bias_tiles(p, a.bias, nullptr, bias_k, s)) != hipSuccess) return e;
+  if (fused) {
     if ((e = launch_bwd_fused(p, a, bias_k, s)) != hipSuccess) return e;
   } else {
-    if ((e = launch_bias_tiles(p, a.bias, bias_q, bias_k, s)) != hipSuccess) return e;
     if ((e = launch_dq_pipe(p, a, bias_q, s)) != hipSuccess) return e;
     if ((e = launch_dkdv_pipe(p, a, bias_k, s)) != hipSuccess) return e;
   }

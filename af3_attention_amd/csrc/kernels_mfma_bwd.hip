@@ -42,8 +42,11 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restri
   }
 }
 
-// Per-row terms of the backward, one thread per (r, j, h) in memory order (so a
-// wave reads contiguous 2*d-byte pieces of O and dO), D = sum_c dout[r,j,h,c] o[r,j,h,c]:
+// Per-row terms of the backward, one thread per (r, j, h): in memory order (h,
+// then j fastest) for the [R, N, H, d] layout, so that a wave reads contiguous
+// pieces of O and dO; in the order (r, h, j), j fastest, for the transposed
+// layout, where memory order would scatter every operand write (a lane still
+// reads the 2*d contiguous bytes of its query).  D = sum_c dout[r,j,h,c] o[r,j,h,c]:
 //   qops[r,h,j]  = the complete query-side operands of the S and dP steps
 //                  (-sqrt(d) lse and -D, split; dbias and the fused kernel)
 //   qaug[r,h,j]  = the same in the packed form of the dq and dkdv kernels (only
@@ -64,11 +67,19 @@ __global__ __launch_bounds__(256) void bwd_rowterms_kernel(Problem p, BwdArgs a,
   const int64_t idx = static_cast<int64_t>(blockIdx.x - tiles) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(p.R) * p.H * p.N;
   if (idx >= total) return;
-  const int h = static_cast<int>(idx % p.H);
-  const int64_t pr = idx / p.H;  // (r, j) or (j, r) in memory order
-  const int r = static_cast<int>(p.transpose ? pr % p.R : pr / p.N);
-  const int j = static_cast<int>(p.transpose ? pr / p.R : pr % p.N);
-  const int64_t off = idx * D;
+  int r, j, h;
+  if (p.transpose) {
+    j = static_cast<int>(idx % p.N);
+    const int64_t rh_idx = idx / p.N;
+    h = static_cast<int>(rh_idx % p.H);
+    r = static_cast<int>(rh_idx / p.H);
+  } else {
+    h = static_cast<int>(idx % p.H);
+    const int64_t rj = idx / p.H;
+    j = static_cast<int>(rj % p.N);
+    r = static_cast<int>(rj / p.N);
+  }
+  const int64_t off = elem_offset(p, r, j, h);
   const u32x4* o = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.o) + off);
   const u32x4* d = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dout) + off);
   float s = 0.f;

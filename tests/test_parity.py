@@ -47,6 +47,18 @@ def test_bf16_ragged_triangle(R, N, H, D, transpose):
     compare(gpu_fwd_bwd(inp), oracle_fwd_bwd(inp), "bf16", transpose)
 
 
+@pytest.mark.parametrize("R,N,H,D,transpose", [(150, 100, 2, 32, 0), (150, 100, 2, 32, 1), (200, 20, 3, 16, 0),
+                                                 (200, 20, 3, 16, 1), (130, 257, 4, 32, 0), (300, 72, 4, 8, 0)])
+def test_bf16_rows_per_workgroup(R, N, H, D, transpose):
+    """More (row, head) pairs than compute units, so the persistent fused backward's
+    workgroups walk several rows (row changes with a ragged last key tile, one key
+    tile only, and d = 8 and 16)."""
+    banner(f"bf16 rows per workgroup R={R} N={N} H={H} D={D} t={transpose}")
+    inp = generate(R, N, H, D, dtype=torch.bfloat16, transpose=transpose, bias_std=math.sqrt(2),
+                   mask_kind="tail_uniform", mask_frac=0.15, seed=R * 3 + N + D)
+    compare(gpu_fwd_bwd(inp), oracle_fwd_bwd(inp), "bf16", transpose)
+
+
 @pytest.mark.parametrize("transpose", [0, 1])
 def test_bwd_ignores_workspace_contents(transpose):
     """The backward's workspace (tiled bias copies, per-row operands, dBias partial

@@ -10,9 +10,10 @@
 // partial sums that a last pass adds in increasing group order.
 //
 // Per row the workgroup stages Q, dO (its 128 queries), K, V (its 128 keys) and
-// the row's split lse, D and mask operands in LDS with direct copies, through a ring of four
-// stages (two at d = 64; copies run that many rows ahead minus one).  The 8 waves split the tile into 4 key tiles x 2
-// query halves; a wave owns 32 keys and two 32-query tiles:
+// the row's pre-formed lse, D and mask operands in LDS with direct copies, through
+// a ring of four stages (two at d = 64; copies run that many rows ahead minus
+// one).  A wave owns 32 keys and one (d >= 32: 16 waves) or two (8 waves) 32-query
+// tiles:
 //   S  = Q K^T + sqrt(d) bias + sqrt(d) (mask - lse)   (bias: accumulator input;
 //        mask and lse: one extra MFMA step on split-bf16 operands)
 //   dP = dO V^T - D                                   (D: one extra MFMA step)
@@ -30,14 +31,21 @@ using namespace mfma;
 using namespace pipe;
 
 constexpr int kDbT = 128;      // tile edge (queries and keys)
-constexpr int kDbThreads = 512;  // 8 waves: 4 key tiles x 2 query halves
+// Waves: 4 key tiles x 4 query tiles, one 32 x 32 tile each (four waves per SIMD
+// hide more of each tile's dependency chain) for d >= 32; 4 key tiles x 2 query
+// halves, two tiles each, at smaller d, where the shorter MFMA chains leave the
+// exp work dominant and fewer waves with two independent tiles measured faster.
+template <int D>
+constexpr int db_tpw() { return D >= 32 ? 1 : 2; }  // query tiles per wave
+template <int D>
+constexpr int db_threads() { return 64 * 4 * (4 / db_tpw<D>()); }
 // LDS ring of rows (copies run db_stages - 1 rows ahead): four stages of 38 KB
 // up to d = 32, two of 70 KB at d = 64.
 template <int D>
 constexpr int db_stages() { return D >= 64 ? 2 : 4; }
 
 template <int D>
-__global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, BwdArgs a,
+__global__ __launch_bounds__(db_threads<D>(), 1) void dbias_pipe_kernel(Problem p, BwdArgs a,
                                                                    const float* __restrict__ bias_k, int nt,
                                                                    int groups, float* __restrict__ out) {
   constexpr int TB = Tile<D, kDbT>::BYTES;
@@ -46,7 +54,8 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
   constexpr int NS = db_stages<D>();
   constexpr int DUMMY = NS * STAGE;  // 1 KB target of dummy copies
   constexpr int KS = Shape<D>::KS;
-  using St = Stager<D, 2, kDbT, kDbThreads>;
+  constexpr int TPW = db_tpw<D>();
+  using St = Stager<D, 2, kDbT, db_threads<D>()>;
   constexpr int NROW = 2 * St::NIT + 1;  // copies per thread per row: Q/dO, K/V, one operand piece
   __shared__ __align__(16) char lds[NS * STAGE + 1024];
 
@@ -59,7 +68,7 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
   const int g = blk % groups;
   const int h = blk / groups;
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int wk = wave & 3, wq = wave >> 2;  // key tile, query half of this wave
+  const int wk = wave & 3, wq = wave >> 2;  // key tile, query group of this wave
   const int q0 = qb * kDbT, k0 = kb * kDbT;
 
   const int rows_per = (p.R + groups - 1) / groups;
@@ -77,10 +86,10 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
 
   // sqrt(d) * bias of this wave's 32 keys and two 32-query tiles: constant over
   // the rows, so it is loaded once.
-  f32x16 bias[2], acc[2];
+  f32x16 bias[TPW], acc[TPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    bias[t] = load_bias_tile(bias_k + bias_tile_offset(h, qb * 4 + 2 * wq + t, kb * 4 + wk, nt), lane);
+  for (int t = 0; t < TPW; ++t) {
+    bias[t] = load_bias_tile(bias_k + bias_tile_offset(h, qb * 4 + TPW * wq + t, kb * 4 + wk, nt), lane);
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
   }
@@ -143,8 +152,8 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
     if (lane >> 5) s_key = u32x4{0u, 0u, 0u, 0u};
 
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int x0 = (2 * wq + t) * 32;      // first query of this tile within the block
+    for (int t = 0; t < TPW; ++t) {
+      const int x0 = (TPW * wq + t) * 32;      // first query of this tile within the block
       const int jl = x0 + (lane & 31);       // this lane's query (as an A-operand row)
       const u32x4 s_q = lds_load16(stats + (jl >> 5) * 1024 + (jl & 31) * 16);
       const u32x4 dp_q = lds_load16(stats + (jl >> 5) * 1024 + 512 + (jl & 31) * 16);
@@ -163,8 +172,8 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
 
   // Prologue: the bias tiles have arrived, then rows r_begin .. r_begin + NS - 2
   // go into stages 0 .. NS - 2.
-  retire(bias[0]);
-  retire(bias[1]);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) retire(bias[t]);
   if (r_begin < r_end) issue_row(r_begin, std::integral_constant<int, 0>());
   if constexpr (NS > 2) {
     if (r_begin + 1 < r_end) issue_row(r_begin + 1, std::integral_constant<int, 1>());
@@ -184,10 +193,10 @@ __global__ __launch_bounds__(kDbThreads, 1) void dbias_pipe_kernel(Problem p, Bw
   if (key >= p.N) return;
   float* dst = out + (static_cast<int64_t>(g) * p.H + h) * p.N * p.N + key;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int j = q0 + (2 * wq + t) * 32 + acc_row(v, lane);
+      const int j = q0 + (TPW * wq + t) * 32 + acc_row(v, lane);
       if (j < p.N) dst[static_cast<int64_t>(j) * p.N] = acc[t][v];
     }
 }
@@ -223,16 +232,16 @@ hipError_t launch_dbias_pipe(const Problem& p, const BwdArgs& a, const float* bi
   KernelTimer timer("bwd_dbias_mfma", s);
   switch (p.D) {
     case 8:
-      hipLaunchKernelGGL((dbias_pipe_kernel<8>), dim3(blocks), dim3(kDbThreads), 0, s, p, a, bias_k, nt, groups, out);
+      hipLaunchKernelGGL((dbias_pipe_kernel<8>), dim3(blocks), dim3(db_threads<8>()), 0, s, p, a, bias_k, nt, groups, out);
       break;
     case 16:
-      hipLaunchKernelGGL((dbias_pipe_kernel<16>), dim3(blocks), dim3(kDbThreads), 0, s, p, a, bias_k, nt, groups, out);
+      hipLaunchKernelGGL((dbias_pipe_kernel<16>), dim3(blocks), dim3(db_threads<16>()), 0, s, p, a, bias_k, nt, groups, out);
       break;
     case 32:
-      hipLaunchKernelGGL((dbias_pipe_kernel<32>), dim3(blocks), dim3(kDbThreads), 0, s, p, a, bias_k, nt, groups, out);
+      hipLaunchKernelGGL((dbias_pipe_kernel<32>), dim3(blocks), dim3(db_threads<32>()), 0, s, p, a, bias_k, nt, groups, out);
       break;
     case 64:
-      hipLaunchKernelGGL((dbias_pipe_kernel<64>), dim3(blocks), dim3(kDbThreads), 0, s, p, a, bias_k, nt, groups, out);
+      hipLaunchKernelGGL((dbias_pipe_kernel<64>), dim3(blocks), dim3(db_threads<64>()), 0, s, p, a, bias_k, nt, groups, out);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -142,14 +142,20 @@ __global__ __launch_bounds__(db_threads<D>(), 1) void dbias_pipe_kernel(Problem 
     const uint32_t stats = st + 4 * TB;
     const int kl = wk * 32 + (lane & 31);  // this lane's key within the tile
 
-    u32x4 kop[KS], vop[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kop[ks] = rd.rows_operand(tk, wk * 32, ks, lane);
-      vop[ks] = rd.rows_operand(tv, wk * 32, ks, lane);
-    }
     u32x4 s_key = lds_load16(stats + 2 * kDbT * 16 + kl * 16);
-    if (lane >> 5) s_key = u32x4{0u, 0u, 0u, 0u};
+    u32x4 kop[KS], vop[KS];
+    if constexpr (D == 8) {
+      // The per-row terms ride in k slots 8..15 (lanes 32..63) of the one MFMA step.
+      kop[0] = rd.rows_operand_with(tk, wk * 32, lane, s_key);
+      vop[0] = rd.rows_operand_with(tv, wk * 32, lane, u32x4{kBf16One | (kBf16One << 16), kBf16One, 0u, 0u});
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kop[ks] = rd.rows_operand(tk, wk * 32, ks, lane);
+        vop[ks] = rd.rows_operand(tv, wk * 32, ks, lane);
+      }
+      if (lane >> 5) s_key = u32x4{0u, 0u, 0u, 0u};
+    }
 
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -157,14 +163,20 @@ __global__ __launch_bounds__(db_threads<D>(), 1) void dbias_pipe_kernel(Problem 
       const int jl = x0 + (lane & 31);       // this lane's query (as an A-operand row)
       const u32x4 s_q = lds_load16(stats + (jl >> 5) * 1024 + (jl & 31) * 16);
       const u32x4 dp_q = lds_load16(stats + (jl >> 5) * 1024 + 512 + (jl & 31) * 16);
-      f32x16 sacc = mma(rd.rows_operand(tq, x0, 0, lane), kop[0], bias[t]);
+      f32x16 sacc, dp;
+      if constexpr (D == 8) {
+        sacc = mma(rd.rows_operand_with(tq, x0, lane, s_q), kop[0], bias[t]);
+        dp = mma(rd.rows_operand_with(tdo, x0, lane, dp_q), vop[0], f32x16{});
+      } else {
+        sacc = mma(rd.rows_operand(tq, x0, 0, lane), kop[0], bias[t]);
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tq, x0, ks, lane), kop[ks], sacc);
-      sacc = mma(s_q, s_key, sacc);
-      f32x16 dp = mma(rd.rows_operand(tdo, x0, 0, lane), vop[0], f32x16{});
+        for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tq, x0, ks, lane), kop[ks], sacc);
+        sacc = mma(s_q, s_key, sacc);
+        dp = mma(rd.rows_operand(tdo, x0, 0, lane), vop[0], f32x16{});
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tdo, x0, ks, lane), vop[ks], dp);
-      dp = mma(dp_q, dp_key, dp);
+        for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tdo, x0, ks, lane), vop[ks], dp);
+        dp = mma(dp_q, dp_key, dp);
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][e] = __builtin_fmaf(fast_exp2(sacc[e] * c1), dp[e], acc[t][e]);
     }

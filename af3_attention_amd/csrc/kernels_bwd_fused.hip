@@ -137,7 +137,8 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
   const uint16_t* const dop = static_cast<const uint16_t*>(a.dout);
   const uint16_t* const kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* const vp = static_cast<const uint16_t*>(a.v);
-  const u32x4 dp_key = key_aug_unit(lane);
+  // Key side of the D step (at d = 8 in every lane: it rides in k slots 8..15).
+  const u32x4 dp_key = D == 8 ? u32x4{kBf16One | (kBf16One << 16), kBf16One, 0u, 0u} : key_aug_unit(lane);
 
   // Tile A: w (w < 4) or w + 4; tile B: w + 4 (w < 4 only).  Invalid tiles (past
   // the row's keys) run on clamped, finite data and are never stored.
@@ -148,7 +149,8 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
   tb.valid = pair_wave && tb.kt < nkt;
   // The mask value of the lane's key in row r, loaded ahead; when the row starts
   // it becomes the key-side split operand [1, 1, 1, m, m, m, 0, 0] (m = sqrt(d)
-  // mask split in three; zeros in lanes 32..63).
+  // mask split in three; zeros in lanes 32..63, except at d = 8 where the operand
+  // rides in the k slots 8..15 of the product's own MFMA step).
   auto load_key_side = [&](KeyTile& t, int r) __attribute__((always_inline)) {
     const int key = min(t.kt * 32 + (lane & 31), p.N - 1);
     t.mask_next = a.mask ? a.mask[static_cast<int64_t>(r) * p.N + key] : 0.f;
@@ -156,8 +158,8 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
   auto start_tile = [&](KeyTile& t) __attribute__((always_inline)) {
     retire(t.mask_next);
     const Split3 sm = split3(fmaxf(sd * t.mask_next, -kHuge));
-    t.s_key = half ? u32x4{0u, 0u, 0u, 0u}
-                   : u32x4{kBf16One | (kBf16One << 16), kBf16One | (sm.hi << 16), sm.mid | (sm.lo << 16), 0u};
+    const u32x4 op = {kBf16One | (kBf16One << 16), kBf16One | (sm.hi << 16), sm.mid | (sm.lo << 16), 0u};
+    t.s_key = (half && D != 8) ? u32x4{0u, 0u, 0u, 0u} : op;
 #pragma unroll
     for (int e = 0; e < 16; ++e) t.dk[e] = t.dv[e] = 0.f;
   };
@@ -271,6 +273,12 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
     const u32x4 s_q = lds_load16(st + 2 * TQ + jl * 16);
     const u32x4 dp_q = lds_load16(st + 2 * TQ + 512 + jl * 16);
     const uint32_t kt_lds = kres + t.kt * (32 * 2 * D), vt_lds = kt_lds + KRES;
+    if constexpr (D == 8) {
+      // The per-row terms ride in k slots 8..15 of the one MFMA step.
+      sacc = mma(rd.rows_operand_with(tq, 0, lane, s_q), rd.rows_operand_with(kt_lds, 0, lane, t.s_key), sacc);
+      return mma(rd.rows_operand_with(tdo, 0, lane, dp_q), rd.rows_operand_with(vt_lds, 0, lane, dp_key),
+                 f32x16{});
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       sacc = mma(rd.rows_operand(tq, 0, ks, lane), rd.rows_operand(kt_lds, 0, ks, lane), sacc);

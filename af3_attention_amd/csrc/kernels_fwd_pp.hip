@@ -154,6 +154,10 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
       dst[0][ks] = global_operand<D>(p, qp, it.r0, j, it.h, ks, half);
       dst[1][ks] = global_operand<D>(p, qp, it.r1, j, it.h, ks, half);
     }
+    if constexpr (D == 8 && MASKED) {
+      // k slots 8..15 (lanes 32..63) carry the query side of the mask step.
+      if (half) dst[0][0] = dst[1][0] = mask_query_side(0);
+    }
   };
 
   St st;
@@ -267,12 +271,20 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
     constexpr int i = decltype(i_c)::value;
     constexpr int TIB = decltype(tib_c)::value;
     lds_char* kt = lds_ptr(stage(sc).kv) + (2 * i) * TB;
+    if constexpr (D == 8 && MASKED) {
+      // At d = 8 the mask operand rides in k slots 8..15 (lanes 32..63) of the
+      // logits' one MFMA step.
+      const u32x4 kv = ld16(kt + rd.rows[0] + 32 * TIB * (2 * D));
+      const u32x4 ka = ld16(lds_ptr(stage(sc).kaug) + (i * kBlk + 32 * TIB + (lane & 31)) * 16);
+      ops.k[0] = half ? ka : kv;
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ops.k[ks] = rd.rows_operand(kt, 32 * TIB, ks, lane);
-    // (lanes 32..63 hold k slots 8..15, zero on the query side: they read 16 zero
-    // bytes, since a masked key's operand holds -inf)
-    if constexpr (MASKED)
-      ops.ka = ld16(half ? lds_ptr(zero16) : lds_ptr(stage(sc).kaug) + (i * kBlk + 32 * TIB + (lane & 31)) * 16);
+      for (int ks = 0; ks < KS; ++ks) ops.k[ks] = rd.rows_operand(kt, 32 * TIB, ks, lane);
+      // (lanes 32..63 hold k slots 8..15, zero on the query side: they read 16 zero
+      // bytes, since a masked key's operand holds -inf)
+      if constexpr (MASKED)
+        ops.ka = ld16(half ? lds_ptr(zero16) : lds_ptr(stage(sc).kaug) + (i * kBlk + 32 * TIB + (lane & 31)) * 16);
+    }
   };
   // Logits of row I for the tile in ops into S[I] (accumulator input c = bias).
   auto logits = [&](auto i_c, const f32x16& c) __attribute__((always_inline)) {
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
     f32x16 acc = mma(ops.k[0], qreg[i][0], c);
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks) acc = mma(ops.k[ks], qreg[i][ks], acc);
-    if constexpr (MASKED) acc = mma(ops.ka, mq, acc);
+    if constexpr (MASKED && D != 8) acc = mma(ops.ka, mq, acc);
     S[i] = acc;
   };
   // O^T of row I += V^T P^T for the tile in ops.

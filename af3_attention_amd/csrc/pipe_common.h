@@ -181,6 +181,14 @@ struct TileReads {
     if (D < 16 && (lane >> 5)) return u32x4{0u, 0u, 0u, 0u};
     return v;
   }
+  // At d = 8 the operand's k slots 8..15 (lanes 32..63) are free: the same read,
+  // with `extra` in those lanes (for instance the split operands of the per-row
+  // terms, so that they ride in the same MFMA).
+  __device__ __forceinline__ u32x4 rows_operand_with(uint32_t tile, int x0, int lane, u32x4 extra) const {
+    static_assert(D == 8, "k slots 8..15 are free only at d = 8");
+    const u32x4 v = lds_load16(tile + rows[0] + x0 * (2 * D));
+    return (lane >> 5) ? extra : v;
+  }
   // A operand: rows = channels 32 db + (lane & 31), k = 16 positions p0 + 16 t + the
   // permutation of MFMA accumulator registers 8t..8t+7 (ds_read_b64_tr_b16), so
   // those registers of a tile whose rows are the positions p0.., packed to bf16,

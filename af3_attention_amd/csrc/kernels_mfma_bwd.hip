@@ -42,81 +42,116 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restri
   }
 }
 
-// Per-row terms of the backward, one thread per (r, j, h): in memory order (h,
-// then j fastest) for the [R, N, H, d] layout, so that a wave reads contiguous
-// pieces of O and dO; in the order (r, h, j), j fastest, for the transposed
-// layout, where memory order would scatter every operand write (a lane still
-// reads the 2*d contiguous bytes of its query).  D = sum_c dout[r,j,h,c] o[r,j,h,c]:
+// Per-row terms of the backward, D = sum_c dout[r,j,h,c] o[r,j,h,c]:
 //   qops[r,h,j]  = the complete query-side operands of the S and dP steps
 //                  (-sqrt(d) lse and -D, split; dbias and the fused kernel)
 //   qaug[r,h,j]  = the same in the packed form of the dq and dkdv kernels (only
 //                  when those run)
-//   kaug[r,j]    = the key-side split operands of sqrt(d) mask (threads with h = 0)
-// (layouts of the operands: pipe_common.h).
+//   kaug[r,j]    = the key-side split operands of sqrt(d) mask (h = 0)
+// (layouts of the operands: pipe_common.h).  One thread per (r, j, h):
+//  * [R, N, H, d] layout with H in {1, 2, 4, 8} ("staged"): a workgroup takes
+//    256 / H consecutive queries of one row with all heads, so it reads one
+//    contiguous piece of O and dO; the operands go through LDS and leave as
+//    contiguous runs per head;
+//  * otherwise the order (r, h, j), j fastest (a lane reads the 2 d contiguous
+//    bytes of its query, and operand writes are contiguous in j).
 // The same launch also forms the sqrt(d) * bias tiles the later kernels read:
 // blocks 0 .. tiles - 1 each form one tile (pipe::bias_tile), so that this small
 // pass overlaps the row terms instead of taking a launch of its own.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowterms_kernel(Problem p, BwdArgs a, float* __restrict__ bias_q,
-                                                           float* __restrict__ bias_k, int nt, int tiles) {
+                                                           float* __restrict__ bias_k, int nt, int tiles,
+                                                           bool staged) {
   using namespace pipe;
   if (static_cast<int>(blockIdx.x) < tiles) {
     bias_tile(p, static_cast<const uint16_t*>(a.bias), bias_q, bias_k, nt, blockIdx.x);
     return;
   }
-  const int64_t idx = static_cast<int64_t>(blockIdx.x - tiles) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(p.R) * p.H * p.N;
-  if (idx >= total) return;
-  int r, j, h;
-  if (p.transpose) {
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) - tiles;
+  const int t = threadIdx.x;
+  int r, j, h, jq = 0, j0 = 0;  // jq: queries per workgroup (staged)
+  bool valid;
+  if (staged) {
+    jq = 256 / p.H;
+    const int chunks = (p.N + jq - 1) / jq;
+    r = static_cast<int>(blk / chunks);
+    j0 = static_cast<int>(blk % chunks) * jq;
+    j = j0 + t / p.H;
+    h = t % p.H;
+    valid = j < p.N;
+  } else {
+    const int64_t idx = blk * 256 + t;
+    valid = idx < static_cast<int64_t>(p.R) * p.H * p.N;
     j = static_cast<int>(idx % p.N);
     const int64_t rh_idx = idx / p.N;
     h = static_cast<int>(rh_idx % p.H);
     r = static_cast<int>(rh_idx / p.H);
-  } else {
-    h = static_cast<int>(idx % p.H);
-    const int64_t rj = idx / p.H;
-    j = static_cast<int>(rj % p.N);
-    r = static_cast<int>(rj / p.N);
   }
-  const int64_t off = elem_offset(p, r, j, h);
-  const u32x4* o = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.o) + off);
-  const u32x4* d = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dout) + off);
-  float s = 0.f;
+  const float sd = sqrtf(static_cast<float>(D));
+  const int np = qops_queries(p.N);
+  u32x4 sq{}, dq{}, qa{};
+  if (valid) {
+    const int64_t off = elem_offset(p, r, j, h);
+    const u32x4* o = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.o) + off);
+    const u32x4* d = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.dout) + off);
+    float s = 0.f;
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 x = o[c], y = d[c];
+    for (int c = 0; c < D / 8; ++c) {
+      const u32x4 x = o[c], y = d[c];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s += __uint_as_float(x[i] << 16) * __uint_as_float(y[i] << 16);
-      s += __uint_as_float(x[i] & 0xffff0000u) * __uint_as_float(y[i] & 0xffff0000u);
+      for (int i = 0; i < 4; ++i) {
+        s += __uint_as_float(x[i] << 16) * __uint_as_float(y[i] << 16);
+        s += __uint_as_float(x[i] & 0xffff0000u) * __uint_as_float(y[i] & 0xffff0000u);
+      }
+    }
+    const int64_t rhj = (static_cast<int64_t>(r) * p.H + h) * p.N + j;
+    const Split3 na = split3(-lse_term(a.lse[rhj], sd, true));
+    const Split3 nd = split3(-s);
+    qa = u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), nd.hi | (nd.mid << 16), nd.lo};
+    sq = u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), kBf16One | (kBf16One << 16), 0u};
+    dq = u32x4{nd.hi | (nd.mid << 16), nd.lo, 0u, 0u};
+    u32x4* qo = reinterpret_cast<u32x4*>(a.qops) + 2 * (static_cast<int64_t>(r) * p.H + h) * np;
+    if (!staged) {
+      if (a.qaug) reinterpret_cast<u32x4*>(a.qaug)[rhj] = qa;
+      qo[(j >> 5) * 64 + (j & 31)] = sq;
+      qo[(j >> 5) * 64 + 32 + (j & 31)] = dq;
+    }
+    // The padding queries N .. Np - 1 of the row get the dead-query side (every
+    // probability 0) from the thread of query N - 1.
+    if (j == p.N - 1)
+      for (int jj = p.N; jj < np; ++jj) {
+        qo[(jj >> 5) * 64 + (jj & 31)] = dead_query_aug();
+        qo[(jj >> 5) * 64 + 32 + (jj & 31)] = u32x4{0u, 0u, 0u, 0u};
+      }
+    if (h == 0) {
+      const float m = a.mask ? a.mask[static_cast<int64_t>(r) * p.N + j] : 0.f;
+      const Split3 sm = split3(fmaxf(sd * m, -kHuge));
+      reinterpret_cast<u32x4*>(a.kaug)[static_cast<int64_t>(r) * p.N + j] =
+          u32x4{kBf16One | (kBf16One << 16), kBf16One | (sm.hi << 16), sm.mid | (sm.lo << 16), 0u};
     }
   }
-  const int64_t rhj = (static_cast<int64_t>(r) * p.H + h) * p.N + j;
-  const float sd = sqrtf(static_cast<float>(D));
-  const Split3 na = split3(-lse_term(a.lse[rhj], sd, true));
-  const Split3 nd = split3(-s);
-  if (a.qaug)
-    reinterpret_cast<u32x4*>(a.qaug)[rhj] =
-        u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), nd.hi | (nd.mid << 16), nd.lo};
-  // The per-query operands complete (layout: qops_queries): the S step's query
-  // side and the dP step's; the padding queries N .. Np - 1 of the row get the
-  // dead-query side (every probability 0) from the thread of query N - 1.
-  const int np = qops_queries(p.N);
-  u32x4* qo = reinterpret_cast<u32x4*>(a.qops) + 2 * (static_cast<int64_t>(r) * p.H + h) * np;
-  auto put = [&](int jj, u32x4 sq, u32x4 dq) {
-    qo[(jj >> 5) * 64 + (jj & 31)] = sq;
-    qo[(jj >> 5) * 64 + 32 + (jj & 31)] = dq;
-  };
-  put(j, u32x4{na.hi | (na.mid << 16), na.lo | (kBf16One << 16), kBf16One | (kBf16One << 16), 0u},
-      u32x4{nd.hi | (nd.mid << 16), nd.lo, 0u, 0u});
-  if (j == p.N - 1)
-    for (int jj = p.N; jj < np; ++jj) put(jj, dead_query_aug(), u32x4{0u, 0u, 0u, 0u});
-  if (h == 0) {
-    const float m = a.mask ? a.mask[static_cast<int64_t>(r) * p.N + j] : 0.f;
-    const Split3 sm = split3(fmaxf(sd * m, -kHuge));
-    reinterpret_cast<u32x4*>(a.kaug)[static_cast<int64_t>(r) * p.N + j] =
-        u32x4{kBf16One | (kBf16One << 16), kBf16One | (sm.hi << 16), sm.mid | (sm.lo << 16), 0u};
+  if (!staged) return;
+  // Staged: through LDS, [h][query] per operand, then out as contiguous runs.
+  __shared__ u32x4 st_s[256], st_d[256], st_q[256];
+  const int slot = h * jq + (j - j0);
+  st_s[slot] = sq;
+  st_d[slot] = dq;
+  st_q[slot] = qa;
+  __syncthreads();
+  // qops: per head the jq queries are jq / 32 whole blocks, 2 jq consecutive entries.
+#pragma unroll
+  for (int e = t; e < 512; e += 256) {
+    const int hh = e / (2 * jq), w = e % (2 * jq);
+    const int jl = (w >> 6) * 32 + (w & 31);
+    if (j0 + jl < p.N) {
+      u32x4* qo = reinterpret_cast<u32x4*>(a.qops) + 2 * (static_cast<int64_t>(r) * p.H + hh) * np;
+      qo[(j0 >> 5) * 64 + w] = (w & 32) ? st_d[hh * jq + jl] : st_s[hh * jq + jl];
+    }
+  }
+  if (a.qaug) {
+    const int hh = t / jq, jl = t % jq;
+    if (j0 + jl < p.N)
+      reinterpret_cast<u32x4*>(a.qaug)[(static_cast<int64_t>(r) * p.H + hh) * p.N + j0 + jl] = st_q[hh * jq + jl];
   }
 }
 
@@ -135,9 +170,12 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_q, 
     const int64_t rows_total = static_cast<int64_t>(p.R) * p.H * p.N;
     const int nt = bias_tiles(p.N);
     const int tiles = p.H * nt * nt;
+    const bool staged = !p.transpose && (p.H == 1 || p.H == 2 || p.H == 4 || p.H == 8);
+    const int64_t row_blocks = staged ? static_cast<int64_t>(p.R) * ((p.N + 256 / p.H - 1) / (256 / p.H))
+                                      : (rows_total + 255) / 256;
     KernelTimer timer("bwd_prep", s);
-    hipLaunchKernelGGL((bwd_rowterms_kernel<D>), dim3(static_cast<unsigned>(tiles + (rows_total + 255) / 256)),
-                       dim3(256), 0, s, p, a, fused ? nullptr : bias_q, bias_k, nt, tiles);
+    hipLaunchKernelGGL((bwd_rowterms_kernel<D>), dim3(static_cast<unsigned>(tiles + row_blocks)), dim3(256), 0, s, p,
+                       a, fused ? nullptr : bias_q, bias_k, nt, tiles, staged);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (fused) {

@@ -12,21 +12,25 @@
 // The unit of work is one attention row r of one head h with all its keys, so
 // every sum above completes inside one workgroup and nothing is accumulated
 // across workgroups.  The grid is persistent: one workgroup per compute unit
-// walks through its rows one after another, and the copies of the next row's K
-// and V (into a second buffer), of its first query block and of its key-side
-// operands are issued during the current row's last block, so a workgroup never
-// waits for a row to start.
+// walks through its rows one after another.  The next row's K and V are copied
+// into a second buffer in pieces over the current row's first blocks, and its
+// first query block and mask values during the current row, so a workgroup never
+// waits for a row to start; each workgroup starts its rows at a different query
+// block, so that the row changes of different compute units fall at different
+// times.
 //  * 8 waves, two per SIMD.  The 12 key tiles of 32 keys are split so that each
 //    SIMD carries three: wave w < 4 owns tiles w and w + 4, wave w >= 4 owns tile
 //    w + 4 and also forms dQ (below).  Each wave keeps its tiles' dK, dV in
 //    registers while the workgroup walks the row's queries in blocks of 32, and
-//    stores them at the start of the next row.  Q, dO and the per-query operands
-//    of each block are staged by direct copies, double buffered;
+//    stores them at the start of the next row (through LDS, as whole key rows).
+//    Q, dO and the per-query operands of each block are staged by direct copies,
+//    double buffered;
 //  * tiles are S = Q K^T (queries x keys), so a lane holds one key:
 //      S  = Q K^T + sqrt(d) bias + sqrt(d) (mask - lse)   (bias: accumulator input,
-//           a tiled fp32 copy loaded one block ahead; mask and lse: one extra
-//           MFMA step on split-bf16 operands)
-//      dP = dO V^T - D                                   (D: one extra MFMA step)
+//           a tiled fp32 copy loaded one block ahead, S accumulating in place in
+//           its registers; mask and lse: one extra MFMA step on split-bf16
+//           operands, at d = 8 folded into the free k slots of the main step)
+//      dP = dO V^T - D                                   (D: likewise)
 //      P = exp2(S log2(e)/sqrt(d)),  dS = P dP
 //    P and dS, packed to bf16 in registers, are the B operands of dV^T += dO^T P
 //    and dK^T += Q^T dS (A operands: transposing LDS reads of dO and Q);

@@ -125,12 +125,32 @@ def recorded_traffic(kernel, workload):
     return None
 
 
+def warm_up(step, args, sync):
+    """The --warmup untimed steps, then more until --min-warmup-ms of wall time has
+    passed.  Returns (extra steps, warm-up seconds)."""
+    t0 = time.perf_counter()
+    for _ in range(args.warmup):
+        step()
+    sync()
+    extra = 0
+    while (time.perf_counter() - t0) * 1e3 < args.min_warmup_ms:
+        for _ in range(5):
+            step()
+        sync()
+        extra += 5
+    return extra, time.perf_counter() - t0
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first (the GPU clocks take some tens of ms to settle)")
+    ap.add_argument("--min-warmup-ms", type=float, default=300.0,
+                    help="after the --warmup steps, keep running untimed steps until this much wall time of "
+                         "warm-up has passed (the clocks of a GPU that was idle ramp up over the first few "
+                         "hundred ms of work); the extra steps are reported in the JSON line")
     ap.add_argument("--workload", default="tri_start_bf16_n384",
                     help="an attention workload, a layer norm + projection workload "
                          "(pair_proj_bf16_n384, pair_proj_end_bf16_n768, msa_proj_bf16_s512_n384) or a SwiGLU "
@@ -411,9 +431,7 @@ def proj_main(args, w):
         _lib.timing_enable(False)
         return start.elapsed_time(stop) / args.steps, _lib.timing_collect()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_extra, warm_s = warm_up(step, args, torch.cuda.synchronize)
     base_mem = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
     ms, _ = timed(step)
@@ -442,7 +460,7 @@ def proj_main(args, w):
     cpu = None if args.no_cpu_baseline else proj_cpu_baseline(w, inp_cpu, args.cpu_seconds)
     line = {
         "metric": PROJ_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "warmup_extra_steps": warm_extra, "warmup_s": round(warm_s, 3), "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "a": w.a, "b": w.b, "channels": w.channels, "heads": H, "head_dim": D,
                    "qkv": w.qkv, "bias": w.bias, "bias_transpose": bt, "seed": args.seed},
@@ -637,9 +655,7 @@ def transition_main(args, w):
         _lib.timing_enable(False)
         return start.elapsed_time(stop) / args.steps, _lib.timing_collect()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_extra, warm_s = warm_up(step, args, torch.cuda.synchronize)
     base_mem = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
     ms, _ = timed(step)
@@ -663,7 +679,7 @@ def transition_main(args, w):
     cpu = None if args.no_cpu_baseline else transition_cpu_baseline(w, inp_cpu, args.cpu_seconds)
     line = {
         "metric": TRANS_METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "warmup_extra_steps": warm_extra, "warmup_s": round(warm_s, 3), "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "a": w.a, "b": w.b, "channels": w.channels, "expansion": w.expansion,
                    "seed": args.seed},
@@ -718,9 +734,7 @@ def main():
             ea.evoattn_bwd(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], o, lse, inp["dout"],
                            bool(inp["transpose"]))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_extra, warm_s = warm_up(step, args, torch.cuda.synchronize)
     torch.cuda.reset_peak_memory_stats(dev)
     base_mem = torch.cuda.memory_allocated(dev)
 
@@ -803,7 +817,7 @@ def main():
 
     line = {
         "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "warmup_extra_steps": warm_extra, "warmup_s": round(warm_s, 3), "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "rows": w.rows, "n": w.n, "heads": w.heads, "head_dim": w.head_dim,
                    "transpose": variants, "mask": w.mask_kind, "seed": args.seed},

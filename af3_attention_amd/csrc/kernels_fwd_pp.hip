@@ -383,8 +383,9 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
   // loads issued one block earlier are retired (the compiler's own wait for bias
   // registers would drain every outstanding vector memory operation, so each
   // block's global traffic is issued at known points): block b + 1's stage and
-  // the bias of its tiles have arrived; the copies of block b + 2 start (its bias
-  // half a step later, in half-step B).  After the current item's last tile row 0 switches to the next
+  // the bias of its tiles have arrived; the bias of block b + 2's tiles starts
+  // (its copies half a step later, in half-step B, which spreads the
+  // vector-memory issue over the block).  After the current item's last tile row 0 switches to the next
   // item's queries (its logits of the next tile belong to the next item).
   auto half_a = [&](int g, auto ph_c, auto first_c) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph_c)::value;
@@ -400,7 +401,8 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
     if constexpr (PH % 2 == 1) {
       wait_vm<0>();
       lds_barrier();
-      issue_copies((g + 1) / 2 + 1, std::integral_constant<int, ((PH + 1) / 2 + 1) % 4>());
+      load_bias(bias[(PH + 3) % 4], g + 3);
+      load_bias(bias[(PH + 4) % 4], g + 4);
       if (g == 2 * gb_nxt - 1) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qreg[0][ks] = qnext[0][ks];
@@ -423,11 +425,8 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
     softmax(I1());
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (PH % 2 == 1) {
-      // The bias of block b + 2's tiles (their registers were last read by the
-      // logits of this block), issued one half-step after the block's copies so
-      // that the vector-memory issue is spread over the block.
-      load_bias(bias[(PH + 3) % 4], g + 3);
-      load_bias(bias[(PH + 4) % 4], g + 4);
+      // The copies of block b + 2 (into the stage of block b - 2, long free).
+      issue_copies((g + 1) / 2 + 1, std::integral_constant<int, ((PH + 1) / 2 + 1) % 4>());
       if (g == 2 * gb_nxt - 1) {
         finalize(I0(), cur);
 #pragma unroll

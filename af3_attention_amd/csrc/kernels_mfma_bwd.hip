@@ -32,9 +32,32 @@ namespace {
 using namespace mfma;
 
 // dbias[i] = sum over groups g = 0, 1, ... of part[g][i], in increasing g.
+// Each thread takes four consecutive elements (when n is a multiple of 4, so that
+// every group's partial stays 16-byte aligned), issues all groups' loads before
+// the first add (groups <= kMaxDbiasGroups), then adds them in increasing g.
+constexpr int kMaxDbiasGroups = 16;
 __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restrict__ part, int groups, int64_t n,
                                                            float* __restrict__ dbias) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+  const int64_t n4 = n % 4 == 0 ? n / 4 : 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float4 v[kMaxDbiasGroups];
+#pragma unroll
+    for (int g = 0; g < kMaxDbiasGroups; ++g)
+      if (g < groups) v[g] = reinterpret_cast<const float4*>(part + static_cast<int64_t>(g) * n)[i];
+    float4 s = v[0];
+#pragma unroll
+    for (int g = 1; g < kMaxDbiasGroups; ++g)
+      if (g < groups) {
+        s.x += v[g].x;
+        s.y += v[g].y;
+        s.z += v[g].z;
+        s.w += v[g].w;
+      }
+    reinterpret_cast<float4*>(dbias)[i] = s;
+  }
+  // (otherwise one element per thread)
+  for (int64_t i = 4 * n4 + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     float s = part[i];
     for (int g = 1; g < groups; ++g) s += part[static_cast<int64_t>(g) * n + i];

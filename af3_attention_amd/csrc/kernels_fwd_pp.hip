@@ -366,7 +366,10 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
     const bool dead = (i ? it.live1 : it.live0) < 0 || !(l_tot > 0.f);  // every key of the row masked
     const float inv = dead ? 0.f : 1.f / l_tot;
     if (j < p.N && (i == 0 || it.v1)) {
-      store_dT<D>(static_cast<uint16_t*>(a.o) + elem_offset(p, r, j, it.h), &O[i], inv, half);
+      if constexpr (D >= 16)
+        store_dT_x16<D>(static_cast<uint16_t*>(a.o) + elem_offset(p, r, j, it.h), O[i], inv, half);
+      else
+        store_dT<D>(static_cast<uint16_t*>(a.o) + elem_offset(p, r, j, it.h), &O[i], inv, half);
       if (a.lse && half == 0)
         a.lse[(static_cast<int64_t>(r) * p.H + it.h) * p.N + j] =
             dead ? -INFINITY : (m_run[i] + __log2f(l_tot)) * kLn2;

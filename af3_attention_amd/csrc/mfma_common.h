@@ -103,5 +103,26 @@ __device__ __forceinline__ void store_dT(uint16_t* dst_row, const f32x16* acc, f
   }
 }
 
+// The same store with 16-byte pieces (d = 16, 32): lanes l and l + 32 hold the
+// two halves of one position's channels; one v_permlane32_swap per packed dword
+// gives lane l channels 16 pr + 0..7 and lane l + 32 channels 16 pr + 8..15, so a
+// store covers 32 contiguous bytes of each position instead of two 8-byte pieces.
+template <int D>
+__device__ __forceinline__ void store_dT_x16(uint16_t* dst_row, const f32x16& acc, float scale, int half) {
+  static_assert(D == 16 || D == 32, "two channel groups per 16-channel pair");
+#pragma unroll
+  for (int pr = 0; pr < D / 16; ++pr) {
+    const int g0 = 2 * pr, g1 = 2 * pr + 1;
+    const uint32_t a0 = pack_bf16(acc[4 * g0] * scale, acc[4 * g0 + 1] * scale);
+    const uint32_t a1 = pack_bf16(acc[4 * g0 + 2] * scale, acc[4 * g0 + 3] * scale);
+    const uint32_t b0 = pack_bf16(acc[4 * g1] * scale, acc[4 * g1 + 1] * scale);
+    const uint32_t b1 = pack_bf16(acc[4 * g1 + 2] * scale, acc[4 * g1 + 3] * scale);
+    // lanes 0..31: {own, partner's} group g0; lanes 32..63: {partner's, own} group g1
+    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+    *reinterpret_cast<u32x4*>(dst_row + 16 * pr + 8 * half) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+  }
+}
+
 }  // namespace mfma
 }  // namespace evo

@@ -99,27 +99,38 @@ __global__ __launch_bounds__(db_threads<D>(), 1) void dbias_pipe_kernel(Problem 
   const uint16_t* const kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* const vp = static_cast<const uint16_t*>(a.v);
 
-  // Copies of row r into stage s: Q, dO (queries q0..), K, V (keys k0..), and one
+  // Rows are issued in increasing order: running offsets of the next row to issue
+  // (its Q/dO/K/V element offset, this wave's piece of its query operands, its key
+  // operands).
+  int64_t iss_rh = row_head_offset(p, r_begin, h);
+  const int64_t rh_step = p.row_stride * p.H * D;
+  const u32x4* iss_qo = static_cast<const u32x4*>(a.qops) +
+                        2 * (static_cast<int64_t>(r_begin) * p.H + h) * qops_queries(p.N) + 2 * q0 + 64 * (wave & 3);
+  const int64_t qo_step = 2 * static_cast<int64_t>(p.H) * qops_queries(p.N);
+  const u32x4* iss_ka = static_cast<const u32x4*>(a.kaug) + static_cast<int64_t>(r_begin) * p.N;
+  // Copies of the next row into stage s: Q, dO (queries q0..), K, V (keys k0..), and one
   // 64-entry piece of the split operands for each of waves 0..5: the 128 queries'
   // pre-formed operands (4 KB, waves 0..3) and the 128 keys' (2 KB, waves 4, 5).
-  auto issue_row = [&](int r, auto stage_c) {
+  auto issue_row = [&](auto stage_c) {
     constexpr int s = decltype(stage_c)::value;
     const uint32_t st = lds0 + s * STAGE;
-    const int64_t rh = row_head_offset(p, r, h);
+    const int64_t rh = iss_rh;
+    iss_rh += rh_step;
     const char* qd[2] = {uniform_ptr(reinterpret_cast<const char*>(qp + rh)),
                          uniform_ptr(reinterpret_cast<const char*>(dop + rh))};
     const char* kv[2] = {uniform_ptr(reinterpret_cast<const char*>(kp + rh)),
                          uniform_ptr(reinterpret_cast<const char*>(vp + rh))};
     stager.issue(st, qd, q0, p.N, wave, lds0 + DUMMY);
     stager.issue(st + 2 * TB, kv, k0, p.N, wave, lds0 + DUMMY);
+    const u32x4* const qo = iss_qo;
+    const u32x4* const ka = iss_ka;
+    iss_qo += qo_step;
+    iss_ka += p.N;
     if (wave < 4) {
-      const u32x4* qo = static_cast<const u32x4*>(a.qops) +
-                        2 * (static_cast<int64_t>(r) * p.H + h) * qops_queries(p.N) + 2 * q0 + 64 * wave;
       copy16_to_lds(uniform_ptr(qo), static_cast<uint32_t>(lane) * 16, st + 4 * TB + 1024 * wave);
     } else if (wave < 6) {
       const int piece = wave & 1;
-      copy_rows16(static_cast<const u32x4*>(a.kaug) + static_cast<int64_t>(r) * p.N, k0 + 64 * piece, p.N,
-                  st + 4 * TB + 2 * kDbT * 16 + 1024 * piece, lane);
+      copy_rows16(ka, k0 + 64 * piece, p.N, st + 4 * TB + 2 * kDbT * 16 + 1024 * piece, lane);
     } else {  // keep one operand copy per wave and row, so that waits can count them
       copy16_to_lds(uniform_ptr(a.kaug), 0u, lds0 + DUMMY);
     }
@@ -136,7 +147,7 @@ __global__ __launch_bounds__(db_threads<D>(), 1) void dbias_pipe_kernel(Problem 
     else
       wait_vmcnt<0>();
     barrier();
-    if (r + NS - 1 < r_end) issue_row(r + NS - 1, std::integral_constant<int, (s + NS - 1) % NS>());
+    if (r + NS - 1 < r_end) issue_row(std::integral_constant<int, (s + NS - 1) % NS>());
     const uint32_t st = lds0 + s * STAGE;
     const uint32_t tq = st, tdo = st + TB, tk = st + 2 * TB, tv = st + 3 * TB;
     const uint32_t stats = st + 4 * TB;
@@ -168,13 +179,22 @@ __global__ __launch_bounds__(db_threads<D>(), 1) void dbias_pipe_kernel(Problem 
         sacc = mma(rd.rows_operand_with(tq, x0, lane, s_q), kop[0], bias[t]);
         dp = mma(rd.rows_operand_with(tdo, x0, lane, dp_q), vop[0], f32x16{});
       } else {
-        sacc = mma(rd.rows_operand(tq, x0, 0, lane), kop[0], bias[t]);
+        // Every operand read of the tile is issued before its first product (at
+        // d = 64 the operands of both products would not fit in the registers).
+        u32x4 qo[KS], dop[KS];
 #pragma unroll
-        for (int ks = 1; ks < KS; ++ks) sacc = mma(rd.rows_operand(tq, x0, ks, lane), kop[ks], sacc);
+        for (int ks = 0; ks < KS; ++ks) {
+          qo[ks] = rd.rows_operand(tq, x0, ks, lane);
+          dop[ks] = rd.rows_operand(tdo, x0, ks, lane);
+        }
+        if constexpr (D <= 32) __builtin_amdgcn_sched_barrier(0);
+        sacc = mma(qo[0], kop[0], bias[t]);
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) sacc = mma(qo[ks], kop[ks], sacc);
         sacc = mma(s_q, s_key, sacc);
-        dp = mma(rd.rows_operand(tdo, x0, 0, lane), vop[0], f32x16{});
+        dp = mma(dop[0], vop[0], f32x16{});
 #pragma unroll
-        for (int ks = 1; ks < KS; ++ks) dp = mma(rd.rows_operand(tdo, x0, ks, lane), vop[ks], dp);
+        for (int ks = 1; ks < KS; ++ks) dp = mma(dop[ks], vop[ks], dp);
         dp = mma(dp_q, dp_key, dp);
       }
 #pragma unroll
@@ -186,10 +206,10 @@ __global__ __launch_bounds__(db_threads<D>(), 1) void dbias_pipe_kernel(Problem 
   // go into stages 0 .. NS - 2.
 #pragma unroll
   for (int t = 0; t < TPW; ++t) retire(bias[t]);
-  if (r_begin < r_end) issue_row(r_begin, std::integral_constant<int, 0>());
+  if (r_begin < r_end) issue_row(std::integral_constant<int, 0>());
   if constexpr (NS > 2) {
-    if (r_begin + 1 < r_end) issue_row(r_begin + 1, std::integral_constant<int, 1>());
-    if (r_begin + 2 < r_end) issue_row(r_begin + 2, std::integral_constant<int, 2 % NS>());
+    if (r_begin + 1 < r_end) issue_row(std::integral_constant<int, 1>());
+    if (r_begin + 2 < r_end) issue_row(std::integral_constant<int, 2 % NS>());
   }
   for (int r = r_begin; r < r_end; r += NS) {
     step(r, std::integral_constant<int, 0>());

@@ -82,6 +82,8 @@ struct FwdItem {
   bool v1;
   int live0, live1;  // last live key of each row (N - 1 without a mask, -1 if none)
   int nb;
+  int brow;          // tile index (h nt + qt) nt of the bias tile (this wave's query tile qt, key tile 0)
+  int64_t o0, o1;    // element offsets of (r0, position 0, h) and (r1, position 0, h)
 };
 
 template <int D, bool MASKED>
@@ -134,6 +136,9 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
     }
     const int n_eff = min(p.N, (max(it.live0, it.live1) + kBlk) / kBlk * kBlk);
     it.nb = max(2, (n_eff + kBlk - 1) / kBlk);
+    it.brow = (it.h * nt + min(it.qb * (kPpQueries / 32) + wave, nt - 1)) * nt;
+    it.o0 = row_head_offset(p, it.r0, it.h);
+    it.o1 = row_head_offset(p, it.r1, it.h);
     return it;
   };
   auto item_j = [&](const FwdItem& it) __attribute__((always_inline)) {
@@ -141,11 +146,10 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
   };
   // Slabs of K and V of both rows: K r0, V r0, K r1, V r1.
   auto slabs = [&](const FwdItem& it, const char* (&b)[4]) __attribute__((always_inline)) {
-    const int64_t o0 = row_head_offset(p, it.r0, it.h), o1 = row_head_offset(p, it.r1, it.h);
-    b[0] = reinterpret_cast<const char*>(kp + o0);
-    b[1] = reinterpret_cast<const char*>(vp + o0);
-    b[2] = reinterpret_cast<const char*>(kp + o1);
-    b[3] = reinterpret_cast<const char*>(vp + o1);
+    b[0] = reinterpret_cast<const char*>(kp + it.o0);
+    b[1] = reinterpret_cast<const char*>(vp + it.o0);
+    b[2] = reinterpret_cast<const char*>(kp + it.o1);
+    b[3] = reinterpret_cast<const char*>(vp + it.o1);
   };
   auto load_q = [&](const FwdItem& it, u32x4 (&dst)[2][KS]) __attribute__((always_inline)) {
     const int j = item_j(it);
@@ -225,9 +229,8 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
     FwdItem it;
     int lb;
     resolve(gt >> 1, it, lb);
-    const int qt = min(it.qb * (kPpQueries / 32) + wave, nt - 1);
     const int kt = min(2 * lb + (gt & 1), nt - 1);
-    dst = load_tile_acc(bias_t + pipe::bias_tile_offset(it.h, qt, kt, nt), lane);
+    dst = load_tile_acc(bias_t + static_cast<int64_t>(it.brow + kt) * 1024, lane);  // 1024 floats per tile
   };
 
   using I0 = std::integral_constant<int, 0>;

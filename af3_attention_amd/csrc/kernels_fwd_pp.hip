@@ -102,8 +102,10 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
   const int nrg = (p.R + 1) / 2;
   const int nkb = (p.N + kBlk - 1) / kBlk;
   const int wave = pipe::wave_id(), lane = threadIdx.x & 63, half = lane >> 5;
-  const float sd = sqrtf(static_cast<float>(D));
-  const float c1 = kLog2e / sd;
+  // log2(e) / sqrt(d) as a compile-time constant: the logit FMA below then takes it
+  // as an instruction literal (a two-operand encoding that issues faster).
+  static_assert(D == 8 || D == 16 || D == 32, "head_dim");
+  constexpr float c1 = D == 8 ? kLog2e * 0.35355339059327376f : D == 16 ? kLog2e * 0.25f : kLog2e * 0.17677669529663687f;
   const uint16_t* const qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* const kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* const vp = static_cast<const uint16_t*>(a.v);
@@ -247,12 +249,12 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
   u32x4 qreg[2][KS], qnext[2][KS];
   f32x16 S[2], O[2], bias[4];
   u32x4 P[2][2];
-  float m_run[2], l_run[2];
+  float nm_run[2], l_run[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) O[i][e] = 0.f;
-    m_run[i] = 0.f;  // reference point of this query's exponentials, log2 units
+    nm_run[i] = 0.f;  // minus the reference point of this query's exponentials, log2 units
     l_run[i] = 0.f;  // this lane's share of the running sum
   }
 
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
   // yet, so it may also go down) and O, l are rescaled.
   auto softmax = [&](auto i_c) __attribute__((always_inline)) {
     constexpr int i = decltype(i_c)::value;
-    float lsum = exponentiate(i_c, -m_run[i]);
+    float lsum = exponentiate(i_c, nm_run[i]);
     const uint32_t lb = __float_as_uint(l_run[i] + lsum) - 0x1F800000u;  // 2^-64
     schedule_half_step();
     if (__builtin_expect(__ballot(!(lb < 0x40000000u)) != 0, 0)) {       // 2^64 / 2^-64
@@ -349,12 +351,12 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[i][e]);
       mx = pair_max(mx) * c1;
       const bool empty = pair_sum(l_run[i]) == 0.f;
-      const float m_new = empty ? mx : fmaxf(m_run[i], mx);
-      const float alpha = empty || m_new == -INFINITY ? 0.f : fast_exp2(m_run[i] - m_new);
+      const float m_new = empty ? mx : fmaxf(-nm_run[i], mx);
+      const float alpha = empty || m_new == -INFINITY ? 0.f : fast_exp2(-nm_run[i] - m_new);
       l_run[i] *= alpha;
 #pragma unroll
       for (int e = 0; e < 16; ++e) O[i][e] *= alpha;
-      m_run[i] = m_new;
+      nm_run[i] = -m_new;
       lsum = exponentiate(i_c, m_new == -INFINITY ? 0.f : -m_new);  // (no live key yet: every p is 0)
     }
     l_run[i] += lsum;
@@ -375,11 +377,11 @@ __global__ __launch_bounds__(256, 2) void fwd_pp_kernel(Problem p, FwdArgs a, co
         store_dT<D>(static_cast<uint16_t*>(a.o) + elem_offset(p, r, j, it.h), &O[i], inv, half);
       if (a.lse && half == 0)
         a.lse[(static_cast<int64_t>(r) * p.H + it.h) * p.N + j] =
-            dead ? -INFINITY : (m_run[i] + __log2f(l_tot)) * kLn2;
+            dead ? -INFINITY : (__log2f(l_tot) - nm_run[i]) * kLn2;
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) O[i][e] = 0.f;
-    m_run[i] = 0.f;
+    nm_run[i] = 0.f;
     l_run[i] = 0.f;
   };
 

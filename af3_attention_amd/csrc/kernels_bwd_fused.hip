@@ -338,7 +338,9 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
   // The same through LDS (the 2 * 64 * D bytes at reg, free for this wave): the
   // tile is written as [key][channel] bf16 and read back so that each lane
   // stores 16 contiguous bytes and a store covers whole 2 * D-byte key rows
-  // (instead of 8-byte pieces of 32 rows).
+  // (instead of 8-byte pieces of 32 rows).  The 16-byte chunks of key row x sit
+  // in the staged-tile swizzle (chunk c at slot c ^ swz(x)), so the 8-byte writes
+  // of the 32 keys spread over the banks.
   auto store_tile_lds = [&](const Row& w, const KeyTile& t, uint32_t reg) __attribute__((always_inline)) {
     if (!t.valid) return;
     const int x = lane & 31;
@@ -348,23 +350,25 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = 8 * g + 4 * half;
         if (8 * g < D) {
           const f32x16& acc = *accs[m];
-          *reinterpret_cast<lds_u32x2*>(reg + m * 64 * D + x * 2 * D + d * 2) =
+          *reinterpret_cast<lds_u32x2*>(reg + m * 64 * D + x * 2 * D + ((g ^ Tile<D>::swz(x)) * 16) + 8 * half) =
               u32x2{pack_bf16(acc[4 * g] * scales[m], acc[4 * g + 1] * scales[m]),
                     pack_bf16(acc[4 * g + 2] * scales[m], acc[4 * g + 3] * scales[m])};
         }
       }
     }
     uint16_t* const dst[2] = {static_cast<uint16_t*>(a.dv), static_cast<uint16_t*>(a.dk)};
+    int l = lane;
+    asm volatile("" : "+v"(l));  // (per-lane offsets recomputed here, not kept live across rows)
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
       for (int part = 0; part * 1024 < 64 * D; ++part) {
-        const int byte = part * 1024 + lane * 16;
-        const int key = t.kt * 32 + byte / (2 * D), ch = byte % (2 * D) / 2;
-        const u32x4 v = lds_load16(reg + m * 64 * D + byte);
+        const int byte = part * 1024 + l * 16;
+        const int kx = byte / (2 * D), c = byte % (2 * D) / 16;  // key row and 16-byte chunk
+        const int key = t.kt * 32 + kx, ch = 8 * c;
+        const u32x4 v = lds_load16(reg + m * 64 * D + kx * 2 * D + ((c ^ Tile<D>::swz(kx)) * 16));
         if (byte < 64 * D && key < p.N)
           *reinterpret_cast<u32x4*>(dst[m] + elem_offset(p, w.r, key, w.h) + ch) = v;
       }

@@ -164,7 +164,7 @@ def parse():
                     help="after the timed steps, run a plain 256 MiB device copy three times "
                          "(the reference kernel that scales HBM byte counters)")
     ap.add_argument("--memory-curve", action="store_true",
-                    help="instead of the throughput line: peak extra HBM of one fwd+bwd at N = 64 .. 1536 "
+                    help="instead of the throughput line: peak extra HBM of one fwd+bwd at N = 64 .. 2048 "
                          "(R = N, H = 4, d = 32, bf16), beside a materialised fp32 torch reference until it "
                          "runs out of memory")
     ap.add_argument("--no-unfused", action="store_true",
@@ -245,7 +245,7 @@ def memory_curve():
     dev = torch.device("cuda:0")
     out = []
     reference_alive = True
-    for n in (64, 128, 256, 384, 512, 768, 1024, 1536):
+    for n in (64, 128, 256, 384, 512, 768, 1024, 1536, 2048):
         inp = generate(n, n, 4, 32, dtype=torch.bfloat16, bias_std=2 ** 0.5, mask_kind="tail_fixed",
                        mask_frac=0.05, seed=0)
         g = {x: (None if inp[x] is None else inp[x].to(dev)) for x in ("q", "k", "v", "bias", "mask", "dout")}

@@ -185,6 +185,21 @@ def test_full_size_sampled_rows(name, transpose, count):
     print(errs, flush=True)
 
 
+@pytest.mark.parametrize("transpose", [0, 1])
+def test_n2048_sampled_rows(transpose):
+    """N = R = 2048 (the size at which the materialised reference of the memory curve runs
+    out of memory on one MI355X): sampled rows against the oracle."""
+    banner(f"N=2048 transpose={transpose} sampled rows=4")
+    inp = generate(2048, 2048, 4, 32, dtype=torch.bfloat16, transpose=transpose, bias_std=math.sqrt(2.0),
+                   mask_kind="tail_fixed", mask_frac=0.05, seed=transpose)
+    rows = sample_rows(2048, 4)
+    dout = masked_dout(inp["dout"], rows, transpose)
+    got = gpu_fwd_bwd(inp, dout=dout)
+    ref = oracle_fwd_bwd(inp, rows=rows, dout=dout)
+    errs = compare(got, ref, "bf16", transpose, rows=rows)
+    print(errs, flush=True)
+
+
 def test_dbias_bitwise_deterministic():
     """dBias is bit-identical over repeated backward calls, with other work in between."""
     import af3_attention_amd as ea

@@ -90,7 +90,9 @@ struct KeyTile {
 
 template <int D>
 __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdArgs a,
-                                                                  const float* __restrict__ bias_k, int nt) {
+                                                                  const float* __restrict__ bias_k, int nt,
+                                                                  const float* __restrict__ dbias_part,
+                                                                  int dbias_groups) {
   constexpr int KS = Shape<D>::KS;
   static_assert(Shape<D>::DB == 1, "head_dim <= 32");
   constexpr int TQ = Tile<D, kFq>::BYTES;   // one staged tile of 32 queries
@@ -526,21 +528,39 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_fused_kernel(Problem p, BwdA
     run(std::true_type());
   else
     run(std::false_type());
+  // dBias: the dBias pass's partial sums added up in increasing group order, as a
+  // grid-stride pass of this grid once each workgroup's rows are done.
+  if (dbias_part)
+    dbias_reduce_range(dbias_part, dbias_groups, static_cast<int64_t>(p.H) * p.N * p.N, a.dbias,
+                       static_cast<int64_t>(blockIdx.x) * kFThreads + threadIdx.x,
+                       static_cast<int64_t>(gridDim.x) * kFThreads);
 }
 
 }  // namespace
 
 bool bwd_fused_supported(const Problem& p) { return p.D <= 32 && p.N <= kFMaxKeys; }
 
-hipError_t launch_bwd_fused(const Problem& p, const BwdArgs& a, const float* bias_k, hipStream_t s) {
+hipError_t launch_bwd_fused(const Problem& p, const BwdArgs& a, const float* bias_k, const float* dbias_part,
+                            int dbias_groups, hipStream_t s) {
+  if (dbias_part && (a.dbias == nullptr || dbias_groups < 1 || dbias_groups > kMaxDbiasGroups))
+    return hipErrorInvalidValue;
   // Persistent: one workgroup per compute unit (its LDS allows one).
   const int64_t blocks = std::min<int64_t>(static_cast<int64_t>(p.R) * p.H, device_cus());
   const int nt = bias_tiles(p.N);
   KernelTimer timer("bwd_fused_mfma", s);
   switch (p.D) {
-    case 8: hipLaunchKernelGGL((bwd_fused_kernel<8>), dim3(blocks), dim3(kFThreads), 0, s, p, a, bias_k, nt); break;
-    case 16: hipLaunchKernelGGL((bwd_fused_kernel<16>), dim3(blocks), dim3(kFThreads), 0, s, p, a, bias_k, nt); break;
-    case 32: hipLaunchKernelGGL((bwd_fused_kernel<32>), dim3(blocks), dim3(kFThreads), 0, s, p, a, bias_k, nt); break;
+    case 8:
+      hipLaunchKernelGGL((bwd_fused_kernel<8>), dim3(blocks), dim3(kFThreads), 0, s, p, a, bias_k, nt, dbias_part,
+                         dbias_groups);
+      break;
+    case 16:
+      hipLaunchKernelGGL((bwd_fused_kernel<16>), dim3(blocks), dim3(kFThreads), 0, s, p, a, bias_k, nt, dbias_part,
+                         dbias_groups);
+      break;
+    case 32:
+      hipLaunchKernelGGL((bwd_fused_kernel<32>), dim3(blocks), dim3(kFThreads), 0, s, p, a, bias_k, nt, dbias_part,
+                         dbias_groups);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -31,38 +31,12 @@ namespace {
 
 using namespace mfma;
 
-// dbias[i] = sum over groups g = 0, 1, ... of part[g][i], in increasing g.
-// Each thread takes four consecutive elements (when n is a multiple of 4, so that
-// every group's partial stays 16-byte aligned), issues all groups' loads before
-// the first add (groups <= kMaxDbiasGroups), then adds them in increasing g.
-constexpr int kMaxDbiasGroups = 16;
+// dbias[i] = sum over groups g = 0, 1, ... of part[g][i], in increasing g (a
+// grid-stride pass of pipe::dbias_reduce_range).
 __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restrict__ part, int groups, int64_t n,
                                                            float* __restrict__ dbias) {
-  const int64_t n4 = n % 4 == 0 ? n / 4 : 0;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float4 v[kMaxDbiasGroups];
-#pragma unroll
-    for (int g = 0; g < kMaxDbiasGroups; ++g)
-      if (g < groups) v[g] = reinterpret_cast<const float4*>(part + static_cast<int64_t>(g) * n)[i];
-    float4 s = v[0];
-#pragma unroll
-    for (int g = 1; g < kMaxDbiasGroups; ++g)
-      if (g < groups) {
-        s.x += v[g].x;
-        s.y += v[g].y;
-        s.z += v[g].z;
-        s.w += v[g].w;
-      }
-    reinterpret_cast<float4*>(dbias)[i] = s;
-  }
-  // (otherwise one element per thread)
-  for (int64_t i = 4 * n4 + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float s = part[i];
-    for (int g = 1; g < groups; ++g) s += part[static_cast<int64_t>(g) * n + i];
-    dbias[i] = s;
-  }
+  dbias_reduce_range(part, groups, n, dbias, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+                     static_cast<int64_t>(gridDim.x) * blockDim.x);
 }
 
 // Per-row terms of the backward, D = sum_c dout[r,j,h,c] o[r,j,h,c]:
@@ -201,12 +175,16 @@ hipError_t bwd_mfma_dispatch(const Problem& p, const BwdArgs& a, float* bias_q, 
                        a, fused ? nullptr : bias_q, bias_k, nt, tiles, staged);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // The fused pass adds the dBias partials up itself after its rows, so there the
+  // dBias pass runs first; otherwise a separate reduce pass follows it.
+  const bool partials = a.dbias && groups > 1;
   if (fused) {
-    if ((e = launch_bwd_fused(p, a, bias_k, s)) != hipSuccess) return e;
-  } else {
-    if ((e = launch_dq_pipe(p, a, bias_q, s)) != hipSuccess) return e;
-    if ((e = launch_dkdv_pipe(p, a, bias_k, s)) != hipSuccess) return e;
+    if (a.dbias && (e = launch_dbias_pipe(p, a, bias_k, groups, partials ? dbias_part : a.dbias, s)) != hipSuccess)
+      return e;
+    return launch_bwd_fused(p, a, bias_k, partials ? dbias_part : nullptr, groups, s);
   }
+  if ((e = launch_dq_pipe(p, a, bias_q, s)) != hipSuccess) return e;
+  if ((e = launch_dkdv_pipe(p, a, bias_k, s)) != hipSuccess) return e;
   if (a.dbias) {
     float* target = groups == 1 ? a.dbias : dbias_part;
     if ((e = launch_dbias_pipe(p, a, bias_k, groups, target, s)) != hipSuccess) return e;

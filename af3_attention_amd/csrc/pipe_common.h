@@ -390,8 +390,44 @@ __host__ __device__ inline int qops_queries(int n) { return (n + 127) / 128 * 12
 
 // Compute units of the current device (cached per device).
 int device_cus();
+// dbias[i] = sum over groups g = 0, 1, ... of part[g][i], in increasing g, for the
+// elements i = first, first + stride, ... (in units of four elements when n is a
+// multiple of 4, so that every group's partial stays 16-byte aligned).  All groups'
+// loads of an element are issued before the first add (groups <= kMaxDbiasGroups).
+constexpr int kMaxDbiasGroups = 16;
+__device__ __forceinline__ void dbias_reduce_range(const float* __restrict__ part, int groups, int64_t n,
+                                                   float* __restrict__ dbias, int64_t first, int64_t stride) {
+  const int64_t n4 = n % 4 == 0 ? n / 4 : 0;
+  for (int64_t i = first; i < n4; i += stride) {
+    float4 v[kMaxDbiasGroups];
+#pragma unroll
+    for (int g = 0; g < kMaxDbiasGroups; ++g)
+      if (g < groups) v[g] = reinterpret_cast<const float4*>(part + static_cast<int64_t>(g) * n)[i];
+    float4 s = v[0];
+#pragma unroll
+    for (int g = 1; g < kMaxDbiasGroups; ++g)
+      if (g < groups) {
+        s.x += v[g].x;
+        s.y += v[g].y;
+        s.z += v[g].z;
+        s.w += v[g].w;
+      }
+    reinterpret_cast<float4*>(dbias)[i] = s;
+  }
+  // (otherwise one element per thread)
+  for (int64_t i = 4 * n4 + first; i < n; i += stride) {
+    float s = part[i];
+    for (int g = 1; g < groups; ++g) s += part[static_cast<int64_t>(g) * n + i];
+    dbias[i] = s;
+  }
+}
+
 bool bwd_fused_supported(const Problem& p);
-hipError_t launch_bwd_fused(const Problem& p, const BwdArgs& a, const float* bias_k, hipStream_t s);
+// The fused dQ, dK, dV pass.  With dbias_part non-null it also forms a.dbias from
+// the dbias_groups partial sums at dbias_part (the dBias pass runs before it) once
+// its rows are done.
+hipError_t launch_bwd_fused(const Problem& p, const BwdArgs& a, const float* bias_k, const float* dbias_part,
+                            int dbias_groups, hipStream_t s);
 // bf16 forward for head_dim 8, 16, 32 (kernels_fwd_pp.hip).
 hipError_t launch_fwd_pp(const Problem& p, const FwdArgs& a, float* bias_t, void* kaug, int* last_live,
                          hipStream_t s);

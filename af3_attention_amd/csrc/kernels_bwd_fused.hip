@@ -39,7 +39,9 @@
 //    finished query tile over all key tiles with v_mfma_f32_16x16x32_bf16, one
 //    instruction per 32-key tile (A = K^T, read from LDS once per row and kept in
 //    registers; B = dS^T from transposing LDS reads), and stores it.  The dS
-//    tiles are double buffered, so one barrier per block orders everything.
+//    tiles are double buffered, so one barrier per block orders everything;
+//  * when the dBias pass has run first (it writes one partial sum per row group),
+//    the workgroups add those partials up once their rows are done.
 
 #include <algorithm>
 #include <type_traits>

@@ -17,8 +17,9 @@
 //    the keys, and dkdv (kernels_bwd_dkdv.hip), where it owns keys and walks the
 //    queries;
 //  * dbias (kernels_bwd_dbias.hip): a workgroup owns a (query, key) tile of a
-//    head and walks a fixed group of rows; a last pass adds the groups' partial
-//    sums in increasing group order.
+//    head and walks a fixed group of rows; the groups' partial sums are added in
+//    increasing group order by the fused kernel once its rows are done (the dbias
+//    pass then runs before it) or by a last pass after dq and dkdv.
 // Per-row terms (lse, D, the key mask) enter the MFMA accumulators as exact
 // split-bf16 operands prepared once by bwd_rowterms_kernel.
 

@@ -91,6 +91,33 @@ def test_bf16_msa_like_and_other_dims(R, N, H, D):
     compare(gpu_fwd_bwd(inp), oracle_fwd_bwd(inp), "bf16")
 
 
+@pytest.mark.parametrize("R,N,H,D", [(24, 96, 1, 32), (6, 64, 16, 16), (5, 400, 16, 32)])
+def test_bf16_one_and_sixteen_heads(R, N, H, D):
+    banner(f"bf16 heads R={R} N={N} H={H} D={D}")
+    inp = generate(R, N, H, D, dtype=torch.bfloat16, bias_std=math.sqrt(2), mask_kind="tail_uniform",
+                   mask_frac=0.15, seed=R + N + H)
+    compare(gpu_fwd_bwd(inp), oracle_fwd_bwd(inp), "bf16")
+
+
+@pytest.mark.parametrize("R,N,transpose", [(40, 200, 0), (12, 520, 1)])
+def test_bwd_without_dbias_matches(R, N, transpose):
+    """Skipping dBias (as autograd does for a bias that needs no gradient) leaves dQ, dK,
+    dV bit for bit as they are with it, on the fused (N <= 384) and the separate paths."""
+    import af3_attention_amd as ea
+    banner(f"bwd without dBias R={R} N={N} t={transpose}")
+    inp = generate(R, N, 4, 32, dtype=torch.bfloat16, transpose=transpose, bias_std=math.sqrt(2),
+                   mask_kind="tail_uniform", mask_frac=0.15, seed=R + N)
+    g = {x: inp[x].cuda() for x in ("q", "k", "v", "bias", "mask", "dout")}
+    t = bool(transpose)
+    o, lse = ea.evoattn_fwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], t)
+    with_db = ea.evoattn_bwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], o, lse, g["dout"], t, need_dbias=True)
+    without = ea.evoattn_bwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], o, lse, g["dout"], t, need_dbias=False)
+    torch.cuda.synchronize()
+    assert without[3] is None
+    for a, b in zip(with_db[:3], without[:3]):
+        assert torch.equal(a, b)
+
+
 # ---------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("dtype,mode", [(torch.float32, "fp32"), (torch.bfloat16, "bf16")])
